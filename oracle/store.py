@@ -1,0 +1,68 @@
+"""Host model of the paged K/V pool: physical layout, writes and the gather.
+
+Layout (the library's documented pool layout, so that device pools can be
+compared with this model byte for byte):
+    k[block][kv_head][slot_in_block][dim]      ([NB][H_kv][bs][d])
+    v[block][kv_head][dim][slot_in_block]      ([NB][H_kv][d][bs])
+Physical slot s = block * bs + offset holds token position p of a sequence
+whose table maps logical block p // bs to ``block`` and offset = p % bs
+(block table / free pool: Part 8, "Phân Tích Cơ Cấu Bộ Nhớ Của KV Cache"
+diagram; Blog #54, section 2.2). Unwritten slots keep the fill value (NaN in
+tests), which the attention result must never depend on.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .allocator import BlockPoolModel
+
+_NAN_BITS = {"bf16": np.uint16(0x7FC0)}
+
+
+class HostPool:
+    def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int,
+                 head_dim: int, dtype: str, fill_nan: bool = True):
+        self.nb, self.bs, self.hkv, self.d, self.dtype = num_blocks, block_size, num_kv_heads, head_dim, dtype
+        np_t = np.float32 if dtype == "f32" else np.uint16
+        fill = (np.float32(np.nan) if dtype == "f32" else _NAN_BITS["bf16"]) if fill_nan else 0
+        self.k = np.full((num_blocks, num_kv_heads, block_size, head_dim), fill, dtype=np_t)
+        self.v = np.full((num_blocks, num_kv_heads, head_dim, block_size), fill, dtype=np_t)
+
+    def copy_block(self, src: int, dst: int) -> None:
+        self.k[dst] = self.k[src]
+        self.v[dst] = self.v[src]
+
+    def scatter(self, slots, k_new: np.ndarray, v_new: np.ndarray) -> None:
+        """Store token rows k_new/v_new ([n][H_kv][d]) at the given physical slots."""
+        slots = np.asarray(slots, dtype=np.int64)
+        blk, off = slots // self.bs, slots % self.bs
+        # slots are distinct, so the fancy-index assignment has no collisions
+        self.k[blk, :, off, :] = k_new
+        self.v[blk, :, :, off] = v_new
+
+    def write(self, model: BlockPoolModel, table, capacity: int, num_blocks: int,
+              start_pos: int, k_new: np.ndarray, v_new: np.ndarray) -> int:
+        """Append/overwrite tokens of one sequence: allocate and copy-on-write
+        through the allocator model, then store the rows. Returns the new
+        live-block count."""
+        n_live, plan = model.plan_write(table, capacity, num_blocks, start_pos, k_new.shape[0])
+        for src, dst in plan.copies:
+            self.copy_block(src, dst)
+        self.scatter(plan.slots, k_new, v_new)
+        return n_live
+
+    def gather(self, table, ctx_len: int):
+        """Contiguous K, V ([L][H_kv][d]) of a sequence, read through its table."""
+        pos = np.arange(ctx_len)
+        blk = np.asarray(table, dtype=np.int64)[pos // self.bs]
+        off = pos % self.bs
+        k = self.k[blk, :, off, :]                      # [L][H_kv][d]
+        v = self.v[blk, :, :, off]                      # [L][H_kv][d]
+        return k, v
+
+    def gather_head(self, table, ctx_len: int, g: int):
+        """K, V ([L][d]) of KV head g only (bounded memory for long contexts)."""
+        pos = np.arange(ctx_len)
+        blk = np.asarray(table, dtype=np.int64)[pos // self.bs]
+        off = pos % self.bs
+        return self.k[blk, g, off, :], self.v[blk, g, :, off]

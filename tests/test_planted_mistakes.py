@@ -1,0 +1,122 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch each one: a wrong GQA head map, a wrong scale, an off-by-one causal
+bound, K and V swapped, a transposed V slot, a wrong in-block offset, a
+missing softmax normalisation, a merge without the max rescale, a doubled
+byte count, and a FIFO free list."""
+import numpy as np
+import pytest
+
+import oracle.allocator as oalloc
+import oracle.attention as oatt
+import oracle.kvbytes as okv
+import oracle.split as osplit
+import oracle.store as ostore
+from oracle.numerics import to_f64
+from tests import test_oracle_pins as pins
+from tests import test_allocator_model as apins
+
+
+def run_pins():
+    """Run a representative set of pins; return the names of those that fail."""
+    checks = {
+        "brute": lambda: pins.test_oracle_vs_brute_force("bf16", 4, 4, 1, 6, 8, (4, 11, 20)),
+        "brute_gqa": lambda: pins.test_oracle_vs_brute_force("bf16", 1, 8, 2, 4, 4, (3, 8, 13)),
+        "sdpa_verify": lambda: pins.test_oracle_vs_torch_sdpa("prefix_verify"),
+        "sdpa_decode": lambda: pins.test_oracle_vs_torch_sdpa("llama3_8b_decode"),
+        "tables": lambda: [pins.test_printed_block_tables(c) for c in
+                           pins.json.load(open(pins.os.path.join(pins.GOLDEN, "block_tables.json")))["cases"]],
+        "one_token": pins.test_one_token_context_returns_v_exactly,
+        "split": lambda: pins.test_split_merge_equals_direct(512),
+        "kvbytes": lambda: [pins.test_kv_bytes_closed_form(c) for c in
+                            pins.json.load(open(pins.os.path.join(pins.GOLDEN, "kv_bytes.json")))["cases"]],
+        "lifo": apins.test_initial_free_order_and_lifo_reuse,
+        "cow": apins.test_four_samples_share_prompt_then_copy_only_the_diverging_block,
+    }
+    failed = []
+    for name, fn in checks.items():
+        try:
+            fn()
+        except Exception:
+            failed.append(name)
+    return failed
+
+
+def test_pins_pass_on_the_real_oracle():
+    assert run_pins() == []
+
+
+def _seq_mutant(head_map=None, scale_mul=1.0, causal_shift=0, swap_kv=False, normalise=True):
+    def attention_paged_seq(q, pool, table, ctx_len, q_len, num_q_heads, scale):
+        G = num_q_heads // pool.hkv
+        qf = to_f64(q, pool.dtype)
+        out = np.empty(qf.shape)
+        for h in range(num_q_heads):
+            g = head_map(h, G, pool.hkv) if head_map else h // G
+            kr, vr = pool.gather_head(table, ctx_len, g)
+            if swap_kv:
+                kr, vr = vr, kr
+            kf, vf = to_f64(kr, pool.dtype), to_f64(vr, pool.dtype)
+            for i in range(q_len):
+                last = min(ctx_len - 1, ctx_len - q_len + i + causal_shift)
+                s = scale * scale_mul * (kf[:last + 1] @ qf[i, h])
+                e = np.exp(s - s.max())
+                p = e / e.sum() if normalise else e
+                out[i, h] = p @ vf[:last + 1]
+        return out
+    return attention_paged_seq
+
+
+def _gather_mutant(kind):
+    def gather_head(self, table, ctx_len, g):
+        pos = np.arange(ctx_len)
+        blk = np.asarray(table, dtype=np.int64)[pos // self.bs]
+        off = pos % self.bs
+        if kind == "v_transposed":
+            flat = self.v[:, g].transpose(0, 2, 1)          # pretend v were [bs][d] row-major
+            return self.k[blk, g, off, :], flat.reshape(self.nb, self.d, self.bs)[blk, :, off]
+        if kind == "offset":
+            off = (pos // self.bs) % self.bs
+        return self.k[blk, g, off, :], self.v[blk, g, :, off]
+    return gather_head
+
+
+def _merge_no_rescale(m, l, o):
+    w = l
+    return (w[:, :, None] * o).sum(axis=0) / w.sum(axis=0)[:, None]
+
+
+class FifoPool(oalloc.BlockPoolModel):
+    def alloc(self):
+        if not self._stack:
+            raise oalloc.PoolError(oalloc.ERR_NO_FREE_BLOCK)
+        blk = self._stack.pop()
+        self.refcount[blk] = 1
+        return blk
+
+    def free(self, blk):
+        self._check(blk)
+        if self.refcount[blk] == 0:
+            raise oalloc.PoolError(oalloc.ERR_BAD_BLOCK)
+        self.refcount[blk] -= 1
+        if self.refcount[blk] == 0:
+            self._stack.insert(0, blk)                       # tail instead of head
+
+
+MUTANTS = {
+    "head_map_modulo": lambda mp: mp.setattr(oatt, "attention_paged_seq", _seq_mutant(head_map=lambda h, G, H: h % H)),
+    "scale_wrong": lambda mp: mp.setattr(oatt, "attention_paged_seq", _seq_mutant(scale_mul=np.sqrt(2.0))),
+    "causal_off_by_one": lambda mp: mp.setattr(oatt, "attention_paged_seq", _seq_mutant(causal_shift=1)),
+    "k_v_swapped": lambda mp: mp.setattr(oatt, "attention_paged_seq", _seq_mutant(swap_kv=True)),
+    "softmax_unnormalised": lambda mp: mp.setattr(oatt, "attention_paged_seq", _seq_mutant(normalise=False)),
+    "v_layout_transposed": lambda mp: mp.setattr(ostore.HostPool, "gather_head", _gather_mutant("v_transposed")),
+    "in_block_offset": lambda mp: mp.setattr(ostore.HostPool, "gather_head", _gather_mutant("offset")),
+    "merge_without_rescale": lambda mp: mp.setattr(osplit, "lse_merge", _merge_no_rescale),
+    "kv_bytes_doubled": lambda mp: mp.setattr(okv, "kv_bytes_per_token", lambda L, H, d, e: 4 * L * H * d * e),
+    "free_list_fifo": lambda mp: mp.setattr(apins, "BlockPoolModel", FifoPool),
+}
+
+
+@pytest.mark.parametrize("mutant", list(MUTANTS))
+def test_planted_mistake_is_caught(mutant, monkeypatch):
+    MUTANTS[mutant](monkeypatch)
+    assert run_pins(), f"no pin caught the planted mistake {mutant}"
