@@ -1,0 +1,227 @@
+"""Paged decode attention throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--path auto|mfma|valu]
+                    [--partition-tokens N] [--no-cpu-baseline] [--copy-probe]
+
+A step is one pa_attention call over the whole batch of the workload (every
+sequence, every query head), inputs resident in HBM. Default workload: the
+Llama-3-70B-shaped layer, 64 sequences x 8192 tokens, bf16, block size 32.
+Prints one JSON line on stdout; progress goes to stderr.
+
+Algorithmic bytes of a step: every sequence's K and V once
+(sum_b L_b * 2 * H_kv * d * elem), q in and out once (2 * B * q_len * H_q * d
+* elem), the block-table entries read (sum_b ceil(L_b/bs) * 4) and the
+context lengths (4 * B).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+METRIC = "KV GB/s & % of HBM peak; decode tokens/s, 70B-shape layer, 64×8192 ctx"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, lens) -> int:
+    esz = cfg.elem_bytes
+    kv = int(lens.astype(np.int64).sum()) * 2 * cfg.num_kv_heads * cfg.head_dim * esz
+    qo = 2 * cfg.batch * cfg.q_len * cfg.num_q_heads * cfg.head_dim * esz
+    tables = int((-(-lens.astype(np.int64) // cfg.block_size)).sum()) * 4 + 4 * cfg.batch
+    return kv + qo + tables
+
+
+def cpu_baseline(w, budget_s: float = 15.0):
+    """The fp64 oracle (gather through the block table, then the definition)
+    on as many whole sequences as fit in about budget_s seconds."""
+    from oracle import attention as oatt
+    from oracle.build import build_pool
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    cfg = w.cfg
+    log("cpu baseline: building the oracle's host pool")
+    pool, _, tables, _ = build_pool(w, fill_nan=False)
+    done, t_used = 0, 0.0
+    for b in range(cfg.batch):
+        t0 = time.perf_counter()
+        oatt.attention_paged_seq(w.seqs[b].q, pool, tables[b], int(w.lens[b]), cfg.q_len,
+                                 cfg.num_q_heads, cfg.scale)
+        t_used += time.perf_counter() - t0
+        done += 1
+        if t_used >= budget_s:
+            break
+    sub = w.lens[:done]
+    bytes_done = algorithmic_bytes(_sub_cfg(cfg, done), sub)
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {
+        "value": round(bytes_done / t_used / 1e9, 4),
+        "unit": "GB/s",
+        "cores": blas_threads if blas_threads else affinity,
+        "kind": "oracle",
+        "sample": f"{done} of {cfg.batch} sequences (all {cfg.num_q_heads} query heads, full contexts), "
+                  f"{t_used:.1f} s; numpy fp64 with {blas_threads} BLAS threads on {affinity} visible cores",
+        "seconds": round(t_used, 3),
+        "tokens_per_s": round(done * cfg.q_len / t_used, 3),
+    }
+
+
+def _sub_cfg(cfg, batch):
+    from dataclasses import replace
+    return replace(cfg, batch=batch)
+
+
+def copy_probe(gib: float = 1.0, reps: int = 20):
+    """Bandwidth of a plain device-to-device copy (torch's copy kernel)."""
+    import torch
+    n = int(gib * 2**30)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"bytes_read": n, "bytes_written": n, "ms": round(ms, 4),
+            "gbs_read_plus_write": round(2 * n / ms / 1e6, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_70b_decode")
+    ap.add_argument("--path", default="auto", choices=["auto", "mfma", "valu"])
+    ap.add_argument("--partition-tokens", type=int, default=-1,
+                    help="-1: the workload's own setting; 0: library's choice")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md, not implemented)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import paged_kv_cache_218_amd as pa
+    from paged_kv_cache_218_amd.cache import PagedKVCache, lens_to_device, queries_to_device
+
+    cfg = workloads.CONFIGS[args.workload]
+    log(f"generating {cfg.name}")
+    t0 = time.time()
+    w = workloads.generate(cfg, threads=16)
+    log(f"  {time.time() - t0:.1f} s; building the paged cache through pa_write_kv")
+    cache = PagedKVCache.from_workload(w)
+    q = queries_to_device(w)
+    lens_d = lens_to_device(w)
+    tables_d = cache.tables_device()
+    path = {"auto": pa.PA_PATH_AUTO, "mfma": pa.PA_PATH_MFMA, "valu": pa.PA_PATH_VALU}[args.path]
+    pt = cfg.partition_tokens if args.partition_tokens < 0 else args.partition_tokens
+    max_ctx = int(w.lens.max())
+    desc = cache.desc(cfg.num_q_heads, max_ctx, path, pt)
+    plan = pa.pa_attention_plan(desc, cfg.q_len)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step():
+        pa.pa_attention(desc, q, cache.k_pool, cache.v_pool, tables_d, lens_d, cfg.q_len, cfg.scale,
+                        out, ws if plan.workspace_bytes else None, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # HIP events on the stream the kernels are launched on
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / args.steps
+    # per-launch time of the main kernel alone (only separable when there is no merge pass)
+    main_ms = ms if plan.num_partitions == 1 else None
+
+    nbytes = algorithmic_bytes(cfg, w.lens)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tokens = cfg.batch * cfg.q_len / (ms * 1e-3)
+    path_name = {1: "valu", 2: "mfma"}[plan.path]
+    kernel = (f"mfma_attn<{cfg.head_dim},{cfg.block_size},{2 if cfg.group * cfg.q_len > 16 else 1}>"
+              if plan.path == 2 else f"valu_attn<{cfg.dtype},{cfg.head_dim},{cfg.block_size}>")
+    roof_ms = main_ms if main_ms is not None else ms
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1), bf16-rounded; no public dataset)",
+        "config": {
+            "workload": cfg.name, "batch": cfg.batch, "q_len": cfg.q_len,
+            "context_tokens": {"min": int(w.lens.min()), "max": max_ctx, "mean": float(w.lens.mean())},
+            "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
+            "block_size": cfg.block_size, "num_blocks": w.num_blocks, "prefix_len": cfg.prefix_len,
+            "path": path_name, "partition_tokens": plan.partition_tokens,
+            "partitions": plan.num_partitions, "waves_per_group": plan.waves_per_group,
+            "grid": plan.grid, "merge_grid": plan.merge_grid,
+        },
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(tokens, 1),
+        "tokens_per_s_80_layers": round(tokens / 80, 2),
+        "algorithmic_bytes": nbytes,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel,
+            "achieved": round(nbytes / (roof_ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(nbytes / (roof_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "launch_us": round(roof_ms * 1e3, 2),
+            "traffic": None,
+            "note": ("one kernel per step: launch time from HIP events over the timed region"
+                     if main_ms is not None else
+                     "partition kernel + merge kernel per step: time is the pair's"),
+        },
+        "wall_s_timed_region": round(t_wall, 4),
+    }
+    if args.copy_probe:
+        result["copy_probe"] = copy_probe()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,234 @@
+/*
+ * pagedattn.h -- C ABI of libpagedattn.so: a paged KV cache and paged decode
+ * attention for one AMD Instinct MI355X (gfx950).
+ *
+ * The problem, as the pages state it:
+ *   - The KV cache of every sequence is cut into fixed-size physical blocks of
+ *     16 or 32 tokens that may sit anywhere in device memory; a per-sequence
+ *     block table maps logical block j (tokens j*bs .. j*bs+bs-1) to a
+ *     physical block, and the attention kernel reads that table itself.
+ *     [Part 8 (vLLM), "PagedAttention: Ảo Hóa Phân Trang Bộ Nhớ Cho Key và
+ *     Value" and the block-table diagram of "Phân Tích Cơ Cấu Bộ Nhớ Của KV
+ *     Cache"; Blog #54, section 2.2 and its address diagram]
+ *   - A sequence takes one block from the shared free pool each time it grows
+ *     past a multiple of the block size; sequences sharing a prompt point at
+ *     the same blocks with a reference count; a write into a shared block
+ *     first gives the writer a private copy (copy-on-write); a block whose
+ *     count reaches 0 is free again.
+ *     [Blog #54, interview question 2; Part 8, "RadixAttention"]
+ *   - Attention output for query row q_i is softmax(q_i K^T / sqrt(d_k)) V
+ *     over the sequence's context, computed block by block with an online
+ *     softmax. [Part 8, "Thực Thi Kernel Toán Học Trong CUDA", eqs. for A_i,
+ *     A_{i,j} and o_i]
+ *
+ * Conventions for every call:
+ *   - Every call returns a pa_status; nothing throws or aborts across the ABI.
+ *     Argument errors are detected on the host before any state change or
+ *     launch. Device work is asynchronous on the given stream (a hipStream_t
+ *     passed as void*, NULL = the null stream); a fault in it surfaces as
+ *     PA_ERR_HIP from a later launch check or from the caller's own
+ *     synchronisation.
+ *   - "host" pointers are CPU memory, "device" pointers are GPU memory on the
+ *     current HIP device; all buffers are owned by the caller unless stated.
+ *   - Pool layout (device memory, caller-owned, element type = pool dtype):
+ *       k_pool: [num_blocks][num_kv_heads][block_size][head_dim]
+ *       v_pool: [num_blocks][num_kv_heads][head_dim][block_size]
+ *     One (block, kv head) slice of K or V is contiguous (block_size*head_dim
+ *     elements); V keeps each head dimension's tokens adjacent.
+ *   - bf16 is IEEE bfloat16 stored as uint16; f32 is IEEE binary32.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pa_status;
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,   /* bad pointer, shape, range or size */
+  PA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head_dim, block_size, dtype, rows) */
+  PA_ERR_NO_FREE_BLOCK = 3, /* the pool cannot supply the blocks asked for */
+  PA_ERR_BAD_BLOCK = 4,     /* refcount underflow, fork/free of a free block */
+  PA_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
+};
+
+enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
+
+/* Kernel selection for pa_attention. AUTO picks by dtype and row count. */
+enum { PA_PATH_AUTO = 0, PA_PATH_VALU = 1, PA_PATH_MFMA = 2 };
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pa_status_string(pa_status s);
+
+/* ------------------------------------------------------------------------ */
+/* Block pool (host metadata only)                                          */
+/* ------------------------------------------------------------------------ */
+
+typedef struct pa_pool pa_pool;
+
+/* Create the host-side bookkeeping of a pool of num_blocks physical blocks:
+ * a reference count per block (all 0) and a LIFO free list. The free list's
+ * initial order is initial_free_order[0..num_blocks) (host, a permutation of
+ * 0..num_blocks-1; the first entry is handed out first), or ascending ids
+ * when NULL. block_size must be 16 or 32, head_dim 64 or 128, dtype
+ * PA_DTYPE_F32 or PA_DTYPE_BF16 (PA_ERR_UNSUPPORTED otherwise). The device
+ * arrays k_pool/v_pool are not allocated here: the caller owns them.
+ * *out receives the handle (PA_ERR_INVALID_ARG if out is NULL or the order
+ * is not a permutation). [Blog #54 question 2: the free block pool] */
+pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t dtype, const int32_t* initial_free_order,
+                         pa_pool** out);
+
+/* Release the handle (NULL is a no-op). Device memory is not touched. */
+void pa_pool_destroy(pa_pool* pool);
+
+/* Bytes of K plus V that one token occupies: 2 * num_layers * num_kv_heads *
+ * head_dim * elem_bytes; at 16-bit storage this is 4 * L * H_kv * d_k
+ * [Part 8, "Phân Tích Cơ Cấu Bộ Nhớ Của KV Cache": 327,680 B for 80 layers,
+ * 8 KV heads, d_k 128]. Returns -1 if any argument is <= 0. */
+int64_t pa_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t elem_bytes);
+
+/* Pop the head of the free list into *block_id and set its count to 1.
+ * PA_ERR_NO_FREE_BLOCK when the list is empty (state unchanged). */
+pa_status pa_block_alloc(pa_pool* pool, int32_t* block_id);
+
+/* Share a live block: count += 1 [Blog #54 question 2: sharers point at the
+ * same block; Part 8 "RadixAttention": ref_count++ on reuse].
+ * PA_ERR_INVALID_ARG if out of range, PA_ERR_BAD_BLOCK if the block is free. */
+pa_status pa_block_fork(pa_pool* pool, int32_t block_id);
+
+/* Drop one reference; at 0 the block is pushed on the head of the free list
+ * [Part 8 "RadixAttention": blocks with ref_count 0 are reclaimable].
+ * PA_ERR_BAD_BLOCK if the block is already free (state unchanged). */
+pa_status pa_block_free(pa_pool* pool, int32_t block_id);
+
+/* Read-only queries. */
+pa_status pa_block_refcount(const pa_pool* pool, int32_t block_id, int32_t* refcount);
+pa_status pa_pool_num_free(const pa_pool* pool, int32_t* num_free);
+/* Copy the free list, head first, into out[0..capacity) (host); *n receives
+ * its full length. PA_ERR_INVALID_ARG if capacity < length. */
+pa_status pa_pool_free_list(const pa_pool* pool, int32_t* out, int32_t capacity, int32_t* n);
+
+/* ------------------------------------------------------------------------ */
+/* Writing keys and values                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Host-only planning of a write of tokens [start_pos, start_pos + n_tokens)
+ * of one sequence. block_table (host, table_capacity entries) holds the
+ * sequence's physical block ids, the first *num_blocks_inout of them live.
+ * For each logical block the write touches, in ascending order:
+ *   - a block past the live ones is taken from the free list and appended
+ *     [Blog #54 question 2: one new block per block_size tokens];
+ *   - a live block whose count is > 1 is copied into a fresh block, the old
+ *     block loses one reference and the table entry is patched
+ *     (copy-on-write) [Blog #54 question 2: only the diverging part gets a
+ *     new block].
+ * Outputs (host, each nullable): copies_out[2*k], copies_out[2*k+1] = (src,
+ * dst) of the k-th copy, at most max_copies pairs (*n_copies_out = count,
+ * PA_ERR_INVALID_ARG before any change if more would be needed);
+ * slots_out[i] = physical slot (block*block_size + offset) of token
+ * start_pos+i. No device work: the caller must perform the copies before
+ * storing tokens (pa_write_kv does both).
+ * Errors, all before any change: PA_ERR_INVALID_ARG for negative sizes, a
+ * start past the live blocks' end (a hole), or a table too small;
+ * PA_ERR_BAD_BLOCK if a touched live entry names a free block;
+ * PA_ERR_NO_FREE_BLOCK if the pool cannot supply every block needed. */
+pa_status pa_write_plan(pa_pool* pool, int32_t* block_table, int32_t table_capacity,
+                        int32_t* num_blocks_inout, int32_t start_pos, int32_t n_tokens,
+                        int32_t* copies_out, int32_t max_copies, int32_t* n_copies_out,
+                        int32_t* slots_out);
+
+/* Append or overwrite tokens of one sequence: pa_write_plan on the host, then
+ * on `stream` the copy-on-write block copies and one scatter of k_new/v_new
+ * (device, [n_tokens][num_kv_heads][head_dim], pool dtype) into k_pool/v_pool
+ * (device, pool layout above). The host table and live count are updated in
+ * place; the caller re-uploads the table before attention reads it.
+ * Same errors as pa_write_plan (nothing launched), PA_ERR_INVALID_ARG for
+ * NULL device pointers, PA_ERR_HIP if a launch fails (the host state has
+ * then already changed). */
+pa_status pa_write_kv(pa_pool* pool, void* k_pool, void* v_pool, int32_t* block_table_host,
+                      int32_t table_capacity, int32_t* num_blocks_inout, int32_t start_pos,
+                      int32_t n_tokens, const void* k_new, const void* v_new, void* stream);
+
+/* Copy whole physical blocks (every KV head, K and V) on `stream`:
+ * block src_dst[2k] -> block src_dst[2k+1] for k < n_pairs (host array).
+ * The device half of copy-on-write. PA_ERR_INVALID_ARG for an id out of
+ * range or src == dst. */
+pa_status pa_copy_blocks(const pa_pool* pool, void* k_pool, void* v_pool, const int32_t* src_dst,
+                         int32_t n_pairs, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Attention                                                                */
+/* ------------------------------------------------------------------------ */
+
+typedef struct pa_attn_desc {
+  int32_t num_seqs;           /* B */
+  int32_t num_q_heads;        /* H_q, a multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* H_kv; query head h reads KV head h / (H_q/H_kv) */
+  int32_t head_dim;           /* d: 64 or 128 */
+  int32_t block_size;         /* bs: 16 or 32 */
+  int32_t max_blocks_per_seq; /* MB: row stride of block_tables */
+  int32_t num_blocks;         /* NB: pool size; table entries must be in [0, NB) */
+  int32_t dtype;              /* PA_DTYPE_F32 or PA_DTYPE_BF16 (q, pools, out) */
+  int32_t max_context;        /* upper bound on context_lens, <= MB*bs */
+  int32_t path;               /* PA_PATH_* (AUTO unless testing a path) */
+  int32_t partition_tokens;   /* split-KV partition length; 0 = chosen by the library;
+                                 otherwise a positive multiple of 64 */
+  int32_t reserved[5];        /* must be 0 */
+} pa_attn_desc;
+
+/* What pa_attention launches for a descriptor (for tests and profiling). */
+typedef struct pa_attn_plan {
+  int32_t path;               /* PA_PATH_VALU or PA_PATH_MFMA */
+  int32_t partition_tokens;   /* tokens per partition */
+  int32_t num_partitions;     /* partitions per sequence (1 = no merge pass) */
+  int32_t waves_per_group;    /* wavefronts per workgroup of the main kernel */
+  int32_t grid;               /* workgroups of the main kernel */
+  int32_t merge_grid;         /* workgroups of the merge kernel (0 if none) */
+  size_t workspace_bytes;     /* workspace pa_attention needs */
+} pa_attn_plan;
+
+/* Fill *plan for this descriptor and q_len; PA_ERR_INVALID_ARG /
+ * PA_ERR_UNSUPPORTED exactly where pa_attention would fail validation. */
+pa_status pa_attention_plan(const pa_attn_desc* desc, int32_t q_len, pa_attn_plan* plan);
+
+/* Workspace bytes pa_attention needs (0 when no partition merge is needed),
+ * or 0 for an invalid descriptor. */
+size_t pa_attention_workspace_size(const pa_attn_desc* desc, int32_t q_len);
+
+/* Paged attention for q_len query rows per sequence.
+ *   q            device [B][q_len][H_q][d]
+ *   k_pool       device pool layout above; v_pool likewise
+ *   block_tables device int32 [B][max_blocks_per_seq]; entries past a
+ *                sequence's ceil(L_b/bs) blocks are never read
+ *   context_lens device int32 [B]; L_b counts the q_len new tokens, whose
+ *                K/V must already be written at positions L_b-q_len..L_b-1
+ *   q_len        query rows per sequence (1 = decode; > 1 = verification of
+ *                drafted tokens: row i attends to positions 0..L_b-q_len+i)
+ *   scale        multiplies q.k (1/sqrt(d) for standard attention)
+ *   out          device [B][q_len][H_q][d], same dtype as q
+ *   workspace    device, >= pa_attention_workspace_size bytes (may be NULL
+ *                when that is 0); holds split-KV partials, no hidden allocation
+ * Output row (b, i, h) = softmax(scale * q[b,i,h] . K_b[t], t visible) . V_b.
+ * Requirements (else PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED, nothing
+ * launched): H_q % H_kv == 0, d in {64,128}, bs in {16,32}, 1 <= q_len,
+ * max_context <= MB*bs, (H_q/H_kv)*q_len rows within the chosen path's limit.
+ * A sequence whose context_lens entry lies outside [q_len, max_context], or
+ * whose table names a block outside [0, NB), gets NaN in all its output rows;
+ * the kernels never read outside the pools or past a table row. */
+pa_status pa_attention(const pa_attn_desc* desc, const void* q, const void* k_pool,
+                       const void* v_pool, const int32_t* block_tables,
+                       const int32_t* context_lens, int32_t q_len, float scale, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,180 @@
+"""Python names for the C ABI (argument marshalling only).
+
+Each function forwards to the ``pa_*`` entry point of the same name; device
+buffers are torch tensors (their ``data_ptr()`` is passed), host arrays are
+numpy int32 arrays, and the stream defaults to torch's current HIP stream.
+A non-OK status raises ``PAError``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional
+
+import numpy as np
+
+from . import _lib
+from ._lib import AttnDesc, AttnPlan, lib
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib.pa_status_string(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != _lib.PA_OK:
+        raise PAError(status, where)
+
+
+def _i32p(arr: Optional[np.ndarray]):
+    if arr is None:
+        return None
+    assert arr.dtype == np.int32 and arr.flags.c_contiguous
+    return arr.ctypes.data_as(_lib.pi32)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def dtype_code(torch_dtype) -> int:
+    import torch
+    if torch_dtype == torch.float32:
+        return _lib.PA_DTYPE_F32
+    if torch_dtype == torch.bfloat16:
+        return _lib.PA_DTYPE_BF16
+    raise ValueError(f"unsupported dtype {torch_dtype}")
+
+
+# -- pool -------------------------------------------------------------------
+
+class Pool:
+    """Owned pa_pool handle (host metadata only)."""
+
+    def __init__(self, handle: int):
+        self.handle = handle
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            lib.pa_pool_destroy(self.handle)
+            self.handle = None
+
+
+def pa_status_string(status: int) -> str:
+    return lib.pa_status_string(status).decode()
+
+
+def pa_pool_create(num_blocks, block_size, num_kv_heads, head_dim, dtype, initial_free_order=None) -> Pool:
+    out = C.c_void_p()
+    order = None if initial_free_order is None else np.ascontiguousarray(initial_free_order, dtype=np.int32)
+    _check(lib.pa_pool_create(num_blocks, block_size, num_kv_heads, head_dim, dtype, _i32p(order),
+                              C.byref(out)), "pa_pool_create")
+    return Pool(out.value)
+
+
+def pa_kv_bytes_per_token(num_layers, num_kv_heads, head_dim, elem_bytes) -> int:
+    return lib.pa_kv_bytes_per_token(num_layers, num_kv_heads, head_dim, elem_bytes)
+
+
+def pa_block_alloc(pool: Pool) -> int:
+    b = C.c_int32()
+    _check(lib.pa_block_alloc(pool.handle, C.byref(b)), "pa_block_alloc")
+    return b.value
+
+
+def pa_block_fork(pool: Pool, block_id: int) -> None:
+    _check(lib.pa_block_fork(pool.handle, block_id), "pa_block_fork")
+
+
+def pa_block_free(pool: Pool, block_id: int) -> None:
+    _check(lib.pa_block_free(pool.handle, block_id), "pa_block_free")
+
+
+def pa_block_refcount(pool: Pool, block_id: int) -> int:
+    rc = C.c_int32()
+    _check(lib.pa_block_refcount(pool.handle, block_id, C.byref(rc)), "pa_block_refcount")
+    return rc.value
+
+
+def pa_pool_num_free(pool: Pool) -> int:
+    n = C.c_int32()
+    _check(lib.pa_pool_num_free(pool.handle, C.byref(n)), "pa_pool_num_free")
+    return n.value
+
+
+def pa_pool_free_list(pool: Pool) -> np.ndarray:
+    n = C.c_int32()
+    cap = pa_pool_num_free(pool)
+    out = np.zeros(max(cap, 1), dtype=np.int32)
+    _check(lib.pa_pool_free_list(pool.handle, _i32p(out), cap, C.byref(n)), "pa_pool_free_list")
+    return out[:n.value].copy()
+
+
+def pa_write_plan(pool: Pool, block_table: np.ndarray, num_blocks: int, start_pos: int, n_tokens: int,
+                  max_copies: int = 1024):
+    """Returns (new live-block count, copies [(src, dst)], slots[n_tokens]); patches block_table."""
+    live = C.c_int32(num_blocks)
+    copies = np.zeros(2 * max_copies, dtype=np.int32)
+    ncp = C.c_int32()
+    slots = np.zeros(max(n_tokens, 1), dtype=np.int32)
+    _check(lib.pa_write_plan(pool.handle, _i32p(block_table), block_table.size, C.byref(live), start_pos,
+                             n_tokens, _i32p(copies), max_copies, C.byref(ncp), _i32p(slots)),
+           "pa_write_plan")
+    pairs = [(int(copies[2 * k]), int(copies[2 * k + 1])) for k in range(ncp.value)]
+    return live.value, pairs, slots[:n_tokens].copy()
+
+
+def pa_write_kv(pool: Pool, k_pool, v_pool, block_table: np.ndarray, num_blocks: int, start_pos: int,
+                k_new, v_new, stream=None) -> int:
+    """Returns the new live-block count; patches block_table (host int32 row)."""
+    live = C.c_int32(num_blocks)
+    n = 0 if k_new is None else int(k_new.shape[0])
+    _check(lib.pa_write_kv(pool.handle, _ptr(k_pool), _ptr(v_pool), _i32p(block_table), block_table.size,
+                           C.byref(live), start_pos, n, _ptr(k_new), _ptr(v_new), _stream(stream)),
+           "pa_write_kv")
+    return live.value
+
+
+def pa_copy_blocks(pool: Pool, k_pool, v_pool, src_dst: np.ndarray, stream=None) -> None:
+    arr = np.ascontiguousarray(src_dst, dtype=np.int32).reshape(-1)
+    _check(lib.pa_copy_blocks(pool.handle, _ptr(k_pool), _ptr(v_pool), _i32p(arr), arr.size // 2,
+                              _stream(stream)), "pa_copy_blocks")
+
+
+# -- attention ----------------------------------------------------------------
+
+def make_desc(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+              dtype, max_context, path=_lib.PA_PATH_AUTO, partition_tokens=0) -> AttnDesc:
+    d = AttnDesc()
+    d.num_seqs, d.num_q_heads, d.num_kv_heads = num_seqs, num_q_heads, num_kv_heads
+    d.head_dim, d.block_size, d.max_blocks_per_seq = head_dim, block_size, max_blocks_per_seq
+    d.num_blocks, d.dtype, d.max_context = num_blocks, dtype, max_context
+    d.path, d.partition_tokens = path, partition_tokens
+    return d
+
+
+def pa_attention_plan(desc: AttnDesc, q_len: int) -> AttnPlan:
+    plan = AttnPlan()
+    _check(lib.pa_attention_plan(C.byref(desc), q_len, C.byref(plan)), "pa_attention_plan")
+    return plan
+
+
+def pa_attention_workspace_size(desc: AttnDesc, q_len: int) -> int:
+    return int(lib.pa_attention_workspace_size(C.byref(desc), q_len))
+
+
+def pa_attention(desc: AttnDesc, q, k_pool, v_pool, block_tables, context_lens, q_len: int, scale: float,
+                 out, workspace=None, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pa_attention(C.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                            _ptr(context_lens), q_len, scale, _ptr(out), _ptr(workspace), ws_bytes,
+                            _stream(stream)), "pa_attention")

@@ -1,0 +1,124 @@
+"""A batch of sequences over one paged KV pool, driven through the C ABI.
+
+Holds the pool handle (host refcounts and free list), the device K/V pools
+(torch tensors, pool layout k [NB][H_kv][bs][d], v [NB][H_kv][d][bs]), the
+host block tables and each sequence's live-block count. Every operation is
+one ``pa_*`` call; torch only provides the device memory and the stream.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+from . import _lib
+from . import api
+
+
+def _to_device(arr: np.ndarray, torch_dtype, device):
+    import torch
+    if torch_dtype == torch.bfloat16:
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device, non_blocking=False)
+
+
+class PagedKVCache:
+    def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, torch_dtype,
+                 num_seqs: int, max_blocks: int, initial_free_order=None, device="cuda",
+                 fill_nan: bool = True):
+        import torch
+        self.nb, self.bs, self.hkv, self.d = num_blocks, block_size, num_kv_heads, head_dim
+        self.torch_dtype, self.device = torch_dtype, device
+        self.dtype = api.dtype_code(torch_dtype)
+        self.pool = api.pa_pool_create(num_blocks, block_size, num_kv_heads, head_dim, self.dtype,
+                                       initial_free_order)
+        fill = float("nan") if fill_nan else 0.0
+        self.k_pool = torch.full((num_blocks, num_kv_heads, block_size, head_dim), fill,
+                                 dtype=torch_dtype, device=device)
+        self.v_pool = torch.full((num_blocks, num_kv_heads, head_dim, block_size), fill,
+                                 dtype=torch_dtype, device=device)
+        self.tables = np.full((num_seqs, max_blocks), -1, dtype=np.int32)
+        self.live = [0] * num_seqs
+
+    # -- writes -----------------------------------------------------------
+    def write(self, b: int, start_pos: int, k_new, v_new, stream=None) -> None:
+        """Store K/V rows ([n][H_kv][d] device tensors) at positions start_pos.."""
+        row = self.tables[b]          # contiguous view; the library patches it in place
+        self.live[b] = api.pa_write_kv(self.pool, self.k_pool, self.v_pool, row, self.live[b],
+                                       start_pos, k_new, v_new, stream)
+
+    def share_blocks(self, src: int, dst: int, n_blocks: int) -> None:
+        """Sequence dst starts with the first n_blocks blocks of src (forked)."""
+        for j in range(n_blocks):
+            api.pa_block_fork(self.pool, int(self.tables[src, j]))
+            self.tables[dst, j] = self.tables[src, j]
+        self.live[dst] = n_blocks
+
+    def free_seq(self, b: int) -> None:
+        for j in range(self.live[b]):
+            api.pa_block_free(self.pool, int(self.tables[b, j]))
+        self.tables[b, :] = -1
+        self.live[b] = 0
+
+    def tables_device(self):
+        import torch
+        return torch.from_numpy(self.tables).to(self.device)
+
+    # -- attention --------------------------------------------------------
+    def desc(self, num_q_heads: int, max_context: int, path=_lib.PA_PATH_AUTO, partition_tokens=0):
+        return api.make_desc(self.tables.shape[0], num_q_heads, self.hkv, self.d, self.bs,
+                             self.tables.shape[1], self.nb, self.dtype, max_context, path, partition_tokens)
+
+    def attention(self, q, tables_dev, lens_dev, q_len: int, scale: float, max_context: int,
+                  path=_lib.PA_PATH_AUTO, partition_tokens=0, out=None, workspace=None, stream=None):
+        import torch
+        desc = self.desc(q.shape[2], max_context, path, partition_tokens)
+        if out is None:
+            out = torch.empty_like(q)
+        need = api.pa_attention_workspace_size(desc, q_len)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        api.pa_attention(desc, q, self.k_pool, self.v_pool, tables_dev, lens_dev, q_len, scale, out,
+                         workspace, stream)
+        return out
+
+    # -- a whole synthetic batch ---------------------------------------------
+    @classmethod
+    def from_workload(cls, w, device="cuda", shared_prefix: bool = True, fill_nan: bool = True):
+        """Build the cache for a generated workload in its fixed order: with a
+        shared prefix, sequence 0 writes it and the others fork its blocks;
+        then each sequence writes its own tokens after the prefix."""
+        import torch
+        cfg = w.cfg
+        tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+        c = cls(w.num_blocks, cfg.block_size, cfg.num_kv_heads, cfg.head_dim, tdt, cfg.batch,
+                w.max_blocks, w.free_order, device, fill_nan)
+        if cfg.prefix_len:
+            pk, pv = _to_device(w.prefix_k, tdt, device), _to_device(w.prefix_v, tdt, device)
+            if shared_prefix:
+                c.write(0, 0, pk, pv)
+                nblk = math.ceil(cfg.prefix_len / cfg.block_size)
+                for b in range(1, cfg.batch):
+                    c.share_blocks(0, b, nblk)
+            else:
+                for b in range(cfg.batch):
+                    c.write(b, 0, pk, pv)
+        for b in range(cfg.batch):
+            s = w.seqs[b]
+            c.write(b, cfg.prefix_len, _to_device(s.k, tdt, device), _to_device(s.v, tdt, device))
+        return c
+
+
+def queries_to_device(w, device="cuda"):
+    """[B][q_len][H_q][d] query tensor of a workload on the device."""
+    import torch
+    tdt = torch.float32 if w.cfg.dtype == "f32" else torch.bfloat16
+    return _to_device(w.q_all(), tdt, device)
+
+
+def lens_to_device(w, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(w.lens, dtype=np.int32)).to(device)

@@ -1,0 +1,165 @@
+// Device half of writing the paged KV cache: the copy-on-write block copy and
+// the scatter of new tokens' K/V rows into their physical slots.
+//
+// Blog #54, interview question 2: a growing sequence gets a new block per
+// block_size tokens, and a write into a block shared by several sequences
+// first gives the writer its own copy; the host plan (pool.cpp) takes those
+// decisions, these kernels move the bytes.
+//
+// Pool layout: k_pool [NB][H_kv][bs][d], v_pool [NB][H_kv][d][bs].
+// Both kernels take their block ids by value (kernel arguments), so a write
+// needs no device-side staging buffer.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kIdsPerLaunch = 64;    // logical blocks covered by one scatter launch
+constexpr int kPairsPerLaunch = 32;  // block copies per copy launch
+
+struct BlockIds {
+  int32_t id[kIdsPerLaunch];
+};
+struct CopyPairs {
+  int32_t src[kPairsPerLaunch];
+  int32_t dst[kPairsPerLaunch];
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One thread per (token, kv head, 16-byte chunk of the head dim).
+// Token i of this launch is sequence position pos0 + i; its logical block is
+// pos / bs, found at ids.id[pos / bs - first_logical].
+template <typename T>
+__global__ void scatter_kernel(T* __restrict__ k_pool, T* __restrict__ v_pool,
+                               const T* __restrict__ k_new, const T* __restrict__ v_new,
+                               BlockIds ids, int32_t first_logical, int32_t pos0, int32_t tok0,
+                               int32_t n_tok, int32_t hkv, int32_t d, int32_t bs) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int chunks = d / VEC;
+  const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = int64_t(n_tok) * hkv * chunks;
+  if (tid >= total) return;
+  const int c = int(tid % chunks);
+  const int h = int((tid / chunks) % hkv);
+  const int i = int(tid / (int64_t(chunks) * hkv));
+  const int pos = pos0 + i;
+  const int64_t blk = ids.id[pos / bs - first_logical];
+  const int off = pos % bs;
+  const int64_t src = (int64_t(tok0 + i) * hkv + h) * d + int64_t(c) * VEC;
+  // K row: contiguous 16 bytes
+  *reinterpret_cast<u32x4*>(k_pool + ((blk * hkv + h) * bs + off) * d + int64_t(c) * VEC) =
+      *reinterpret_cast<const u32x4*>(k_new + src);
+  // V: element e of the chunk goes to row (c*VEC + e) of the [d][bs] slice
+  T* vdst = v_pool + ((blk * hkv + h) * d + int64_t(c) * VEC) * bs + off;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) vdst[int64_t(e) * bs] = v_new[src + e];
+}
+
+// grid.y = pair index; each thread copies 16 bytes of the K slice and of the V
+// slice of one block (both are block_elems elements long and contiguous).
+template <typename T>
+__global__ void copy_blocks_kernel(T* __restrict__ k_pool, T* __restrict__ v_pool, CopyPairs pairs,
+                                   int64_t block_elems) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int64_t v = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (v * VEC >= block_elems) return;
+  const int64_t s = pairs.src[blockIdx.y] * block_elems + v * VEC;
+  const int64_t t = pairs.dst[blockIdx.y] * block_elems + v * VEC;
+  *reinterpret_cast<u32x4*>(k_pool + t) = *reinterpret_cast<const u32x4*>(k_pool + s);
+  *reinterpret_cast<u32x4*>(v_pool + t) = *reinterpret_cast<const u32x4*>(v_pool + s);
+}
+
+template <typename T>
+pa_status launch_copies(const pa_pool* p, void* k_pool, void* v_pool, const int32_t* src_dst,
+                        int32_t n_pairs, hipStream_t stream) {
+  const int64_t block_elems = int64_t(p->num_kv_heads) * p->block_size * p->head_dim;
+  constexpr int VEC = 16 / sizeof(T);
+  const int threads = 256;
+  const unsigned gx = unsigned((block_elems / VEC + threads - 1) / threads);
+  for (int32_t k0 = 0; k0 < n_pairs; k0 += kPairsPerLaunch) {
+    const int32_t n = std::min<int32_t>(kPairsPerLaunch, n_pairs - k0);
+    CopyPairs cp{};
+    for (int32_t k = 0; k < n; ++k) {
+      cp.src[k] = src_dst[2 * (k0 + k)];
+      cp.dst[k] = src_dst[2 * (k0 + k) + 1];
+    }
+    hipLaunchKernelGGL(copy_blocks_kernel<T>, dim3(gx, n), dim3(threads), 0, stream,
+                       static_cast<T*>(k_pool), static_cast<T*>(v_pool), cp, block_elems);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+template <typename T>
+pa_status launch_scatter(const pa_pool* p, void* k_pool, void* v_pool, const int32_t* table,
+                         int32_t start_pos, int32_t n_tokens, const void* k_new,
+                         const void* v_new, hipStream_t stream) {
+  const int32_t bs = p->block_size, hkv = p->num_kv_heads, d = p->head_dim;
+  constexpr int VEC = 16 / sizeof(T);
+  const int32_t end = start_pos + n_tokens;
+  const int32_t first = start_pos / bs, last = (end - 1) / bs;
+  for (int32_t lb = first; lb <= last; lb += kIdsPerLaunch) {
+    const int32_t lb_end = std::min(last + 1, lb + kIdsPerLaunch);
+    BlockIds ids{};
+    for (int32_t j = lb; j < lb_end; ++j) ids.id[j - lb] = table[j];
+    const int32_t pos0 = std::max(start_pos, lb * bs);
+    const int32_t pos1 = std::min(end, lb_end * bs);
+    const int32_t n = pos1 - pos0;
+    const int64_t total = int64_t(n) * hkv * (d / VEC);
+    const int threads = 256;
+    const unsigned grid = unsigned((total + threads - 1) / threads);
+    hipLaunchKernelGGL(scatter_kernel<T>, dim3(grid), dim3(threads), 0, stream,
+                       static_cast<T*>(k_pool), static_cast<T*>(v_pool),
+                       static_cast<const T*>(k_new), static_cast<const T*>(v_new), ids, lb,
+                       pos0, pos0 - start_pos, n, hkv, d, bs);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_copy_blocks(const pa_pool* pool, void* k_pool, void* v_pool,
+                                    const int32_t* src_dst, int32_t n_pairs, void* stream) {
+  if (!pool || n_pairs < 0 || (n_pairs > 0 && (!k_pool || !v_pool || !src_dst)))
+    return PA_ERR_INVALID_ARG;
+  for (int32_t k = 0; k < 2 * n_pairs; ++k)
+    if (src_dst[k] < 0 || src_dst[k] >= pool->num_blocks) return PA_ERR_INVALID_ARG;
+  for (int32_t k = 0; k < n_pairs; ++k)
+    if (src_dst[2 * k] == src_dst[2 * k + 1]) return PA_ERR_INVALID_ARG;
+  if (n_pairs == 0) return PA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return pool->dtype == PA_DTYPE_F32 ? launch_copies<float>(pool, k_pool, v_pool, src_dst, n_pairs, s)
+                                     : launch_copies<uint16_t>(pool, k_pool, v_pool, src_dst, n_pairs, s);
+}
+
+extern "C" pa_status pa_write_kv(pa_pool* pool, void* k_pool, void* v_pool,
+                                 int32_t* block_table_host, int32_t table_capacity,
+                                 int32_t* num_blocks_inout, int32_t start_pos, int32_t n_tokens,
+                                 const void* k_new, const void* v_new, void* stream) {
+  if (!pool || !block_table_host || !num_blocks_inout) return PA_ERR_INVALID_ARG;
+  if (n_tokens > 0 && (!k_pool || !v_pool || !k_new || !v_new)) return PA_ERR_INVALID_ARG;
+  std::vector<int32_t> copies;
+  pa_status st = pa::plan_write(pool, block_table_host, table_capacity, num_blocks_inout,
+                                start_pos, n_tokens, &copies, INT32_MAX, nullptr);
+  if (st != PA_OK || n_tokens == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t n_pairs = static_cast<int32_t>(copies.size() / 2);
+  if (pool->dtype == PA_DTYPE_F32) {
+    if (n_pairs) st = launch_copies<float>(pool, k_pool, v_pool, copies.data(), n_pairs, s);
+    if (st == PA_OK)
+      st = launch_scatter<float>(pool, k_pool, v_pool, block_table_host, start_pos, n_tokens,
+                                 k_new, v_new, s);
+  } else {
+    if (n_pairs) st = launch_copies<uint16_t>(pool, k_pool, v_pool, copies.data(), n_pairs, s);
+    if (st == PA_OK)
+      st = launch_scatter<uint16_t>(pool, k_pool, v_pool, block_table_host, start_pos, n_tokens,
+                                    k_new, v_new, s);
+  }
+  return st;
+}

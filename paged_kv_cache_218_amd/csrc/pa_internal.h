@@ -1,0 +1,32 @@
+// Internal declarations shared by the host bookkeeping and the HIP launch code.
+#pragma once
+
+#include <cstdint>
+#include <climits>
+#include <vector>
+
+#include "../../include/pagedattn.h"
+
+struct pa_pool {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  int32_t num_kv_heads = 0;
+  int32_t head_dim = 0;
+  int32_t dtype = 0;
+  std::vector<int32_t> refcount;  // per physical block
+  std::vector<int32_t> stack;     // free list; back() is the head
+};
+
+namespace pa {
+
+inline bool supported_block_size(int32_t bs) { return bs == 16 || bs == 32; }
+inline bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
+inline int32_t elem_bytes(int32_t dtype) { return dtype == PA_DTYPE_F32 ? 4 : 2; }
+
+// Host planning of a write (allocation on growth, copy-on-write on shared
+// blocks). copies receives (src, dst) pairs; slots may be null.
+pa_status plan_write(pa_pool* p, int32_t* table, int32_t capacity, int32_t* live_inout,
+                     int32_t start_pos, int32_t n_tokens, std::vector<int32_t>* copies,
+                     int32_t max_copies, int32_t* slots);
+
+}  // namespace pa

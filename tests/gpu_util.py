@@ -1,0 +1,66 @@
+"""Helpers for GPU tests: run the HIP path through the C ABI on a generated
+workload, compute the oracle on the same inputs, compare."""
+import numpy as np
+
+import workloads
+from oracle import attention as oatt
+from oracle.build import build_pool
+from oracle.numerics import to_f64
+
+# tolerances stated for this method: fp32 max |err| <= 1e-5; bf16 max |err|
+# <= 1.5e-2 and mean |err| <= 2e-3, against the fp64 oracle on the same bf16 inputs
+TOL = {"f32": (1e-5, None), "bf16": (1.5e-2, 2e-3)}
+
+
+def out_to_f64(t, dtype):
+    import torch
+    if dtype == "f32":
+        return t.detach().cpu().numpy().astype(np.float64)
+    bits = t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+    return to_f64(bits, "bf16")
+
+
+def out_bits(t):
+    import torch
+    return t.detach().cpu().view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).numpy().copy()
+
+
+def run_gpu(w, path=0, partition_tokens=0, shared_prefix=True, cache=None, q=None, lens=None,
+            max_context=None):
+    import torch
+    from paged_kv_cache_218_amd.cache import PagedKVCache, lens_to_device, queries_to_device
+    cfg = w.cfg
+    if cache is None:
+        cache = PagedKVCache.from_workload(w, shared_prefix=shared_prefix)
+    q = queries_to_device(w) if q is None else q
+    lens_d = lens_to_device(w) if lens is None else lens
+    out = cache.attention(q, cache.tables_device(), lens_d, cfg.q_len, cfg.scale,
+                          max_context or int(w.lens.max()), path=path, partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    return out, cache
+
+
+def oracle_out(w):
+    pool, _, tables, _ = build_pool(w)
+    return oatt.attention_paged(w.q_all(), pool, tables, w.lens, w.cfg.q_len, w.cfg.scale)
+
+
+def oracle_rows(w, seqs):
+    """Oracle for selected sequences, from their contiguous (never-paged) K/V."""
+    cfg = w.cfg
+    res = {}
+    for b in seqs:
+        k, v = w.logical_kv(b)
+        res[b] = oatt.attention_contiguous(w.seqs[b].q, k, v, cfg.q_len, cfg.num_q_heads,
+                                           cfg.num_kv_heads, cfg.scale, cfg.dtype)
+    return res
+
+
+def assert_close(got, ref, dtype, what=""):
+    max_tol, mean_tol = TOL[dtype]
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    assert err.max() <= max_tol, f"{what}: max |err| {err.max():.3g} > {max_tol}"
+    if mean_tol is not None:
+        assert err.mean() <= mean_tol, f"{what}: mean |err| {err.mean():.3g} > {mean_tol}"
+    return float(err.max()), float(err.mean())

@@ -1,0 +1,228 @@
+"""The C-ABI library on the host: exported symbols, the allocator and write
+plan bit-exact against the Python model, error paths and launch planning.
+No device work is done here."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_218_amd as pa
+from paged_kv_cache_218_amd import _lib
+from oracle.allocator import BlockPoolModel, PoolError
+from oracle.build import build_pool
+import workloads
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pagedattn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert "pa_attention" in names and "pa_write_kv" in names and len(names) >= 15
+    for n in names:
+        assert hasattr(_lib.lib, n), n
+    assert sorted(n for n, _, _ in _lib.SIGNATURES) == names
+
+
+def test_status_strings():
+    for s in range(6):
+        assert pa.pa_status_string(s)
+    assert pa.pa_status_string(99) == "unknown status"
+
+
+def test_kv_bytes_per_token_matches_closed_form():
+    assert pa.pa_kv_bytes_per_token(80, 8, 128, 2) == 327680
+    assert pa.pa_kv_bytes_per_token(1, 8, 128, 2) == 4096
+    assert pa.pa_kv_bytes_per_token(32, 8, 128, 4) == 262144
+    assert pa.pa_kv_bytes_per_token(0, 8, 128, 2) == -1
+
+
+def state(pool, nb):
+    return [pa.pa_block_refcount(pool, b) for b in range(nb)], list(pa.pa_pool_free_list(pool))
+
+
+def model_state(m):
+    return list(m.refcount), m.free_list()
+
+
+def test_random_alloc_fork_free_bit_exact():
+    rng = np.random.default_rng(11)
+    nb = 40
+    order = rng.permutation(nb).astype(np.int32)
+    pool = pa.pa_pool_create(nb, 16, 2, 64, pa.PA_DTYPE_BF16, order)
+    m = BlockPoolModel(nb, 16, order)
+    live = []
+    for step in range(3000):
+        op = rng.integers(0, 3)
+        if op == 0:
+            try:
+                want = m.alloc()
+            except PoolError as e:
+                with pytest.raises(pa.PAError) as ex:
+                    pa.pa_block_alloc(pool)
+                assert ex.value.status == e.status
+                continue
+            assert pa.pa_block_alloc(pool) == want
+            live.append(want)
+        elif op == 1 and live:
+            b = int(rng.choice(live))
+            m.fork(b)
+            pa.pa_block_fork(pool, b)
+            live.append(b)
+        elif op == 2 and live:
+            b = live.pop(int(rng.integers(len(live))))
+            m.free(b)
+            pa.pa_block_free(pool, b)
+        if step % 97 == 0:
+            assert state(pool, nb) == model_state(m)
+    assert state(pool, nb) == model_state(m)
+
+
+def test_error_statuses_match_model_and_leave_state():
+    pool = pa.pa_pool_create(3, 16, 2, 64, pa.PA_DTYPE_F32)
+    b = pa.pa_block_alloc(pool)
+    pa.pa_block_free(pool, b)
+    snap = state(pool, 3)
+    for fn, arg, status in [(pa.pa_block_free, b, _lib.PA_ERR_BAD_BLOCK),
+                            (pa.pa_block_fork, b, _lib.PA_ERR_BAD_BLOCK),
+                            (pa.pa_block_free, 7, _lib.PA_ERR_INVALID_ARG),
+                            (pa.pa_block_fork, -1, _lib.PA_ERR_INVALID_ARG)]:
+        with pytest.raises(pa.PAError) as e:
+            fn(pool, arg)
+        assert e.value.status == status
+    assert state(pool, 3) == snap
+    for _ in range(3):
+        pa.pa_block_alloc(pool)
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_block_alloc(pool)
+    assert e.value.status == _lib.PA_ERR_NO_FREE_BLOCK
+
+
+def test_pool_create_validation():
+    for args, status in [((0, 16, 2, 64, 0), _lib.PA_ERR_INVALID_ARG),
+                         ((8, 8, 2, 64, 0), _lib.PA_ERR_UNSUPPORTED),
+                         ((8, 16, 2, 96, 0), _lib.PA_ERR_UNSUPPORTED),
+                         ((8, 16, 2, 64, 5), _lib.PA_ERR_UNSUPPORTED)]:
+        with pytest.raises(pa.PAError) as e:
+            pa.pa_pool_create(*args)
+        assert e.value.status == status
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_pool_create(4, 16, 2, 64, 0, [0, 1, 1, 2])
+    assert e.value.status == _lib.PA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_random_write_plans_bit_exact(seed):
+    """Sequences grow, fork prefixes, overwrite, and free, through both sides."""
+    rng = np.random.default_rng(100 + seed)
+    nb, bs, cap, nseq = 64, 16, 12, 6
+    order = rng.permutation(nb).astype(np.int32)
+    pool = pa.pa_pool_create(nb, bs, 2, 64, pa.PA_DTYPE_BF16, order)
+    m = BlockPoolModel(nb, bs, order)
+    tab_c = np.full((nseq, cap), -1, dtype=np.int32)
+    tab_m = [[-1] * cap for _ in range(nseq)]
+    live = [0] * nseq
+    length = [0] * nseq
+    for step in range(400):
+        s = int(rng.integers(nseq))
+        op = rng.integers(0, 10)
+        if op < 6:       # append or overwrite a few tokens
+            start = int(rng.integers(max(0, length[s] - 20), length[s] + 1))
+            n = int(rng.integers(1, 40))
+            try:
+                lm, plan = m.plan_write(tab_m[s], cap, live[s], start, n)
+            except PoolError as e:
+                row = tab_c[s].copy()
+                with pytest.raises(pa.PAError) as ex:
+                    pa.pa_write_plan(pool, tab_c[s], live[s], start, n)
+                assert ex.value.status == e.status
+                assert np.array_equal(tab_c[s], row)
+                continue
+            lc, copies, slots = pa.pa_write_plan(pool, tab_c[s], live[s], start, n)
+            assert lc == lm and copies == plan.copies and list(slots) == plan.slots
+            live[s] = lm
+            length[s] = max(length[s], start + n)
+        elif op < 8:     # another sequence adopts this one's blocks (prefix sharing)
+            d = int(rng.integers(nseq))
+            if d == s or live[s] == 0:
+                continue
+            for j in range(live[d]):
+                m.free(tab_m[d][j])
+                pa.pa_block_free(pool, int(tab_c[d, j]))
+            for j in range(live[s]):
+                m.fork(tab_m[s][j])
+                pa.pa_block_fork(pool, int(tab_c[s, j]))
+            tab_m[d] = list(tab_m[s])
+            tab_c[d] = tab_c[s]
+            live[d], length[d] = live[s], length[s]
+        else:            # the sequence finishes
+            for j in range(live[s]):
+                m.free(tab_m[s][j])
+                pa.pa_block_free(pool, int(tab_c[s, j]))
+            tab_m[s] = [-1] * cap
+            tab_c[s] = -1
+            live[s] = length[s] = 0
+        assert [list(r[:l]) for r, l in zip(tab_c, live)] == [r[:l] for r, l in zip(tab_m, live)]
+    assert state(pool, nb) == model_state(m)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("prefix_verify", dict(batch=5, prefix_len=40, len_lo=20, len_hi=70)),
+    ("prefix_verify", dict(batch=5, prefix_len=32, len_lo=20, len_hi=70)),
+    ("llama3_8b_decode", dict(batch=6, len_lo=30, len_hi=300)),
+])
+def test_workload_tables_bit_exact(name, kw):
+    """The fixed build order of a workload gives the same tables and refcounts."""
+    w = workloads.generate(workloads.config(name, **kw))
+    cfg = w.cfg
+    _, m, tables, live = build_pool(w)
+    pool = pa.pa_pool_create(w.num_blocks, cfg.block_size, cfg.num_kv_heads, cfg.head_dim,
+                             pa.PA_DTYPE_BF16, w.free_order)
+    tab = np.full((cfg.batch, w.max_blocks), -1, dtype=np.int32)
+    lv = [0] * cfg.batch
+    if cfg.prefix_len:
+        lv[0], _, _ = pa.pa_write_plan(pool, tab[0], 0, 0, cfg.prefix_len)
+        for b in range(1, cfg.batch):
+            for j in range(lv[0]):
+                pa.pa_block_fork(pool, int(tab[0, j]))
+            tab[b, :lv[0]] = tab[0, :lv[0]]
+            lv[b] = lv[0]
+    for b in range(cfg.batch):
+        lv[b], _, _ = pa.pa_write_plan(pool, tab[b], lv[b], cfg.prefix_len, int(w.lens[b]) - cfg.prefix_len)
+    assert np.array_equal(tab, tables) and lv == live
+    assert state(pool, w.num_blocks) == model_state(m)
+
+
+def test_attention_plan_validation():
+    ok = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+              max_blocks_per_seq=8, num_blocks=32, dtype=pa.PA_DTYPE_BF16, max_context=128)
+    pl = pa.pa_attention_plan(pa.make_desc(**ok), 1)
+    assert pl.path == pa.PA_PATH_MFMA and pl.num_partitions >= 1
+    bad = [
+        (dict(num_q_heads=7), 1, _lib.PA_ERR_INVALID_ARG),
+        (dict(head_dim=96), 1, _lib.PA_ERR_UNSUPPORTED),
+        (dict(block_size=8), 1, _lib.PA_ERR_UNSUPPORTED),
+        (dict(max_context=129), 1, _lib.PA_ERR_INVALID_ARG),
+        (dict(), 0, _lib.PA_ERR_INVALID_ARG),
+        (dict(), 129, _lib.PA_ERR_INVALID_ARG),
+        (dict(partition_tokens=100), 1, _lib.PA_ERR_INVALID_ARG),
+        (dict(dtype=7), 1, _lib.PA_ERR_UNSUPPORTED),
+        (dict(num_q_heads=80, num_kv_heads=2), 1, _lib.PA_ERR_UNSUPPORTED),   # 40 rows
+        (dict(dtype=pa.PA_DTYPE_F32, path=pa.PA_PATH_MFMA), 1, _lib.PA_ERR_UNSUPPORTED),
+    ]
+    for over, q_len, status in bad:
+        with pytest.raises(pa.PAError) as e:
+            pa.pa_attention_plan(pa.make_desc(**{**ok, **over}), q_len)
+        assert e.value.status == status, (over, q_len)
+    # the workloads' own partitioning
+    d = pa.make_desc(4, 64, 8, 128, 32, 4096, 16384, pa.PA_DTYPE_BF16, 131072, partition_tokens=512)
+    pl = pa.pa_attention_plan(d, 1)
+    assert (pl.num_partitions, pl.merge_grid) == (256, 4 * 64)
+    assert pl.workspace_bytes == 4 * 64 * 256 * (128 + 2) * 4
+    assert pa.pa_attention_workspace_size(d, 1) == pl.workspace_bytes

@@ -1,0 +1,54 @@
+"""The five workloads at full size on the GPU, in the launch configuration the
+bench times: sampled sequences against the oracle, tables bit-exact."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle.allocator import BlockPoolModel
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+from tests.gpu_util import assert_close, oracle_rows, out_to_f64, run_gpu  # noqa: E402
+
+SAMPLE = {"tiny_f32": None, "llama3_8b_decode": [0, 17, 63], "llama3_70b_decode": [0, 41],
+          "prefix_verify": [0, 64, 127], "long_ctx_split": [3]}
+
+
+def model_tables(w):
+    """Allocation order of the workload replayed on the allocator model (no pool bytes)."""
+    cfg = w.cfg
+    m = BlockPoolModel(w.num_blocks, cfg.block_size, w.free_order)
+    MB = w.max_blocks
+    tabs = [[-1] * MB for _ in range(cfg.batch)]
+    live = [0] * cfg.batch
+    if cfg.prefix_len:
+        live[0], _ = m.plan_write(tabs[0], MB, 0, 0, cfg.prefix_len)
+        for b in range(1, cfg.batch):
+            for j in range(live[0]):
+                m.fork(tabs[0][j])
+                tabs[b][j] = tabs[0][j]
+            live[b] = live[0]
+    for b in range(cfg.batch):
+        live[b], _ = m.plan_write(tabs[b], MB, live[b], cfg.prefix_len, int(w.lens[b]) - cfg.prefix_len)
+    return np.asarray(tabs, dtype=np.int32), m
+
+
+@pytest.mark.parametrize("name", list(SAMPLE))
+def test_full_size(name):
+    import paged_kv_cache_218_amd as pa
+    cfg = workloads.CONFIGS[name]
+    print(f"full-size {name}", flush=True)
+    w = workloads.generate(cfg, threads=16)
+    out, cache = run_gpu(w, partition_tokens=cfg.partition_tokens)
+    tabs, m = model_tables(w)
+    assert np.array_equal(cache.tables, tabs)
+    assert [pa.pa_block_refcount(cache.pool, b) for b in range(w.num_blocks)] == m.refcount
+    if cfg.prefix_len:
+        assert pa.pa_block_refcount(cache.pool, int(tabs[0, 0])) == cfg.batch
+    got = out_to_f64(out, cfg.dtype)
+    seqs = SAMPLE[name] if SAMPLE[name] is not None else range(cfg.batch)
+    ref = oracle_rows(w, seqs)
+    for b in seqs:
+        assert_close(got[b], ref[b], cfg.dtype, f"{name} seq {b}")
+    assert np.isfinite(got).all()

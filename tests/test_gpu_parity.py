@@ -1,0 +1,179 @@
+"""HIP path vs the fp64 oracle through the C ABI (MI355X)."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle.build import build_pool
+from oracle.numerics import to_f64
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from tests.gpu_util import assert_close, oracle_out, oracle_rows, out_bits, out_to_f64, run_gpu  # noqa: E402
+
+VALU, MFMA = 1, 2
+
+SMALL = {
+    "tiny_f32": ("tiny_f32", dict()),
+    "8b": ("llama3_8b_decode", dict(batch=5, len_lo=17, len_hi=700)),
+    "70b": ("llama3_70b_decode", dict(batch=3, len_const=333)),
+    "verify": ("prefix_verify", dict(batch=6, prefix_len=40, len_lo=20, len_hi=300)),
+    "verify_aligned": ("prefix_verify", dict(batch=5, prefix_len=64, len_lo=5, len_hi=200)),
+    "long": ("long_ctx_split", dict(batch=2, len_const=3000)),
+}
+_cache = {}
+
+
+def small(key):
+    if key not in _cache:
+        name, kw = SMALL[key]
+        w = workloads.generate(workloads.config(name, **kw))
+        _cache[key] = (w, oracle_out(w))
+    return _cache[key]
+
+
+CASES = [
+    ("tiny_f32", VALU, 0), ("tiny_f32", VALU, 64),
+    ("8b", MFMA, 0), ("8b", VALU, 0), ("8b", MFMA, 128), ("8b", VALU, 192),
+    ("70b", MFMA, 0), ("70b", VALU, 0), ("70b", MFMA, 64),
+    ("verify", MFMA, 0), ("verify", MFMA, 64), ("verify_aligned", MFMA, 0),
+    ("long", MFMA, 512), ("long", VALU, 512), ("long", MFMA, 0),
+]
+
+
+@pytest.mark.parametrize("key,path,part", CASES, ids=[f"{k}-{'mfma' if p == 2 else 'valu'}-pt{t}" for k, p, t in CASES])
+def test_parity_small(key, path, part):
+    w, ref = small(key)
+    print(f"case {key} path {path} part {part}", flush=True)
+    out, _ = run_gpu(w, path=path, partition_tokens=part)
+    assert_close(out_to_f64(out, w.cfg.dtype), ref, w.cfg.dtype, key)
+
+
+@pytest.mark.parametrize("key", ["8b", "verify", "tiny_f32"])
+def test_pool_bytes_and_tables_match_model(key):
+    """pa_write_kv (allocation, copy-on-write, scatter) gives the model's pool bit for bit."""
+    w, _ = small(key)
+    from paged_kv_cache_218_amd.cache import PagedKVCache
+    import paged_kv_cache_218_amd as pa
+    cache = PagedKVCache.from_workload(w)
+    torch.cuda.synchronize()
+    pool, model, tables, live = build_pool(w)
+    assert np.array_equal(cache.tables, tables) and cache.live == live
+    assert [pa.pa_block_refcount(cache.pool, b) for b in range(w.num_blocks)] == model.refcount
+    assert list(pa.pa_pool_free_list(cache.pool)) == model.free_list()
+    iview = torch.int32 if w.cfg.dtype == "f32" else torch.int16
+    nview = np.int32 if w.cfg.dtype == "f32" else np.int16
+    assert np.array_equal(cache.k_pool.cpu().view(iview).numpy(), pool.k.view(nview))
+    assert np.array_equal(cache.v_pool.cpu().view(iview).numpy(), pool.v.view(nview))
+
+
+def test_copy_blocks_bit_exact():
+    w, _ = small("8b")
+    from paged_kv_cache_218_amd.cache import PagedKVCache
+    import paged_kv_cache_218_amd as pa
+    cache = PagedKVCache.from_workload(w)
+    k0, v0 = cache.k_pool.clone(), cache.v_pool.clone()
+    used = [int(b) for b in cache.tables[0, :cache.live[0]]]
+    free = list(pa.pa_pool_free_list(cache.pool))[:len(used)]
+    pairs = np.array([[s, d] for s, d in zip(used, free)], dtype=np.int32)
+    pa.pa_copy_blocks(cache.pool, cache.k_pool, cache.v_pool, pairs)
+    torch.cuda.synchronize()
+    for s, d in pairs:
+        assert torch.equal(cache.k_pool[d].view(torch.int16), k0[s].view(torch.int16))
+        assert torch.equal(cache.v_pool[d].view(torch.int16), v0[s].view(torch.int16))
+    untouched = [b for b in range(w.num_blocks) if b not in set(pairs[:, 1].tolist())]
+    assert torch.equal(cache.k_pool[untouched].view(torch.int16), k0[untouched].view(torch.int16))
+
+
+@pytest.mark.parametrize("path", [MFMA, VALU])
+def test_permuted_placement_bit_identical(path):
+    w, _ = small("8b")
+    a, _ = run_gpu(w, path=path)
+    w2 = workloads.generate(workloads.config(*[SMALL["8b"][0]], **SMALL["8b"][1]))
+    w2.free_order = np.random.default_rng(77).permutation(w2.num_blocks).astype(np.int32)
+    b, c2 = run_gpu(w2, path=path)
+    assert not np.array_equal(c2.tables, build_pool(w)[2])
+    assert np.array_equal(out_bits(a), out_bits(b))
+
+
+def test_shared_prefix_bit_identical_to_private_copies():
+    w, _ = small("verify")
+    w.num_blocks = w.cfg.batch * w.max_blocks
+    w.free_order = workloads.free_order(w.cfg, w.num_blocks)
+    a, ca = run_gpu(w, shared_prefix=True)
+    b, cb = run_gpu(w, shared_prefix=False)
+    assert np.array_equal(out_bits(a), out_bits(b))
+    import paged_kv_cache_218_amd as pa
+    assert pa.pa_pool_num_free(ca.pool) > pa.pa_pool_num_free(cb.pool)
+
+
+@pytest.mark.parametrize("path", [MFMA, VALU])
+def test_one_token_context_returns_v(path):
+    cfg = workloads.config("llama3_70b_decode", batch=4, lens=(1, 1, 1, 1), len_const=0)
+    w = workloads.generate(cfg)
+    out, _ = run_gpu(w, path=path)
+    got = out.cpu().view(torch.int16).numpy().view(np.uint16)
+    for b in range(4):
+        want = np.repeat(w.seqs[b].v[0], cfg.group, axis=0)
+        assert np.array_equal(got[b, 0], want)
+
+
+def test_causal_rows_ignore_later_tokens():
+    """Row i of a verification call must not see positions after L - q_len + i:
+    overwrite those K/V slots with large values; earlier rows keep their bits."""
+    w, _ = small("verify")
+    cfg = w.cfg
+    out1, cache = run_gpu(w)
+    b, i = 2, 1
+    L = int(w.lens[b])
+    import paged_kv_cache_218_amd as pa
+    n_after = L - (L - cfg.q_len + i + 1)
+    big = torch.full((n_after, cfg.num_kv_heads, cfg.head_dim), 40.0, dtype=torch.bfloat16, device="cuda")
+    cache.write(b, L - n_after, big, -big)
+    out2, _ = run_gpu(w, cache=cache)
+    o1, o2 = out_bits(out1), out_bits(out2)
+    assert np.array_equal(o1[b, :i + 1], o2[b, :i + 1])
+    assert not np.array_equal(o1[b, i + 1:], o2[b, i + 1:])
+    others = [x for x in range(cfg.batch) if x != b]
+    assert np.array_equal(o1[others], o2[others])
+
+
+def test_verify_row_equals_decode_at_its_position():
+    w, _ = small("verify")
+    cfg = w.cfg
+    out, cache = run_gpu(w)
+    got = out_to_f64(out, "bf16")
+    from paged_kv_cache_218_amd.cache import lens_to_device
+    for i in range(cfg.q_len):
+        q_i = torch.from_numpy(np.ascontiguousarray(w.q_all()[:, i:i + 1]).view(np.int16)).view(torch.bfloat16).cuda()
+        lens_i = lens_to_device(w) - (cfg.q_len - 1 - i)
+        o = cache.attention(q_i, cache.tables_device(), lens_i, 1, cfg.scale, int(w.lens.max()))
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(out_to_f64(o, "bf16")[:, 0], got[:, i], rtol=0, atol=1.5e-2)
+
+
+def test_split_matches_unsplit():
+    w, ref = small("long")
+    a, _ = run_gpu(w, partition_tokens=0)
+    for pt in (64, 512, 2048):
+        b, _ = run_gpu(w, partition_tokens=pt)
+        np.testing.assert_allclose(out_to_f64(b, "bf16"), out_to_f64(a, "bf16"), rtol=0, atol=1.5e-2)
+
+
+def test_bad_lengths_and_tables_give_nan_not_faults():
+    w, _ = small("8b")
+    from paged_kv_cache_218_amd.cache import PagedKVCache, lens_to_device
+    cache = PagedKVCache.from_workload(w)
+    lens = lens_to_device(w)
+    lens[1] = int(w.lens.max()) + 5        # beyond max_context
+    lens[2] = 0                           # shorter than q_len
+    tables = cache.tables_device()
+    tables[3, 0] = w.num_blocks + 100     # block id outside the pool
+    for path in (MFMA, VALU):
+        for pt in (0, 128):
+            out = cache.attention(torch.from_numpy(w.q_all().view(np.int16)).view(torch.bfloat16).cuda(),
+                                  tables, lens, 1, w.cfg.scale, int(w.lens.max()), path=path, partition_tokens=pt)
+            torch.cuda.synchronize()
+            o = out_to_f64(out, "bf16")
+            assert np.isnan(o[1]).all() and np.isnan(o[2]).all() and np.isnan(o[3]).all()
+            assert np.isfinite(o[[0, 4]]).all()
