@@ -116,6 +116,7 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "mfma", "valu"])
     ap.add_argument("--partition-tokens", type=int, default=-1,
                     help="-1: the workload's own setting; 0: library's choice")
+    ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup (0: library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
@@ -141,7 +142,7 @@ def main():
     path = {"auto": pa.PA_PATH_AUTO, "mfma": pa.PA_PATH_MFMA, "valu": pa.PA_PATH_VALU}[args.path]
     pt = cfg.partition_tokens if args.partition_tokens < 0 else args.partition_tokens
     max_ctx = int(w.lens.max())
-    desc = cache.desc(cfg.num_q_heads, max_ctx, path, pt)
+    desc = cache.desc(cfg.num_q_heads, max_ctx, path, pt, args.waves)
     plan = pa.pa_attention_plan(desc, cfg.q_len)
     out = torch.empty_like(q)
     ws = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device="cuda")

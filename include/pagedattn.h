@@ -62,6 +62,16 @@ enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
 /* Kernel selection for pa_attention. AUTO picks by dtype and row count. */
 enum { PA_PATH_AUTO = 0, PA_PATH_VALU = 1, PA_PATH_MFMA = 2 };
 
+/* How pa_attention splits the batch's work (reported by pa_attention_plan).
+ * PARTITIONS: one workgroup per (sequence, KV head, fixed-length token
+ *   partition); sequences longer than a partition are finished by a second,
+ *   log-sum-exp merge kernel.
+ * BALANCED: the grid holds as many workgroups as the GPU runs at once and
+ *   each takes an equal share of all (sequence, KV head, 32-token step) work
+ *   items; a sequence split between workgroups is merged by the workgroup
+ *   that finishes its last share (one kernel, no second launch). */
+enum { PA_SCHED_PARTITIONS = 0, PA_SCHED_BALANCED = 1 };
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* pa_status_string(pa_status s);
 
@@ -178,18 +188,23 @@ typedef struct pa_attn_desc {
   int32_t dtype;              /* PA_DTYPE_F32 or PA_DTYPE_BF16 (q, pools, out) */
   int32_t max_context;        /* upper bound on context_lens, <= MB*bs */
   int32_t path;               /* PA_PATH_* (AUTO unless testing a path) */
-  int32_t partition_tokens;   /* split-KV partition length; 0 = chosen by the library;
-                                 otherwise a positive multiple of 64 */
-  int32_t reserved[5];        /* must be 0 */
+  int32_t partition_tokens;   /* 0 = chosen by the library (BALANCED on the MFMA path
+                                 for up to 8192 sequences, else PARTITIONS); otherwise
+                                 PARTITIONS of this many tokens, a multiple of 64 */
+  int32_t waves_per_group;    /* wavefronts per workgroup of the main kernel: 0 = chosen
+                                 by the library, else 1, 2 or 4 */
+  int32_t reserved[4];        /* must be 0 */
 } pa_attn_desc;
 
 /* What pa_attention launches for a descriptor (for tests and profiling). */
 typedef struct pa_attn_plan {
   int32_t path;               /* PA_PATH_VALU or PA_PATH_MFMA */
-  int32_t partition_tokens;   /* tokens per partition */
-  int32_t num_partitions;     /* partitions per sequence (1 = no merge pass) */
+  int32_t schedule;           /* PA_SCHED_PARTITIONS or PA_SCHED_BALANCED */
+  int32_t partition_tokens;   /* PARTITIONS: tokens per partition (0 for BALANCED) */
+  int32_t num_partitions;     /* PARTITIONS: partitions per sequence (1 = no merge pass) */
   int32_t waves_per_group;    /* wavefronts per workgroup of the main kernel */
-  int32_t grid;               /* workgroups of the main kernel */
+  int32_t grid;               /* workgroups of the main kernel (BALANCED: the upper
+                                 bound; the launch uses the device's resident capacity) */
   int32_t merge_grid;         /* workgroups of the merge kernel (0 if none) */
   size_t workspace_bytes;     /* workspace pa_attention needs */
 } pa_attn_plan;
@@ -214,7 +229,11 @@ size_t pa_attention_workspace_size(const pa_attn_desc* desc, int32_t q_len);
  *   scale        multiplies q.k (1/sqrt(d) for standard attention)
  *   out          device [B][q_len][H_q][d], same dtype as q
  *   workspace    device, >= pa_attention_workspace_size bytes (may be NULL
- *                when that is 0); holds split-KV partials, no hidden allocation
+ *                when that is 0); holds split-KV partials, no hidden allocation.
+ *                With the BALANCED schedule its first bytes are arrival
+ *                counters: the workspace must be zero-filled before its first
+ *                use, and every completed call leaves them zero again. Calls
+ *                that share one workspace must not run concurrently.
  * Output row (b, i, h) = softmax(scale * q[b,i,h] . K_b[t], t visible) . V_b.
  * Requirements (else PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED, nothing
  * launched): H_q % H_kv == 0, d in {64,128}, bs in {16,32}, 1 <= q_len,

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedatt
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_NO_FREE_BLOCK, PA_ERR_BAD_BLOCK, PA_ERR_HIP = range(6)
 PA_DTYPE_F32, PA_DTYPE_BF16 = 0, 1
 PA_PATH_AUTO, PA_PATH_VALU, PA_PATH_MFMA = 0, 1, 2
+PA_SCHED_PARTITIONS, PA_SCHED_BALANCED = 0, 1
 
 i32, i64, vp, f32, sz = C.c_int32, C.c_int64, C.c_void_p, C.c_float, C.c_size_t
 pi32 = C.POINTER(C.c_int32)
@@ -22,11 +23,11 @@ class AttnDesc(C.Structure):
     _fields_ = [("num_seqs", i32), ("num_q_heads", i32), ("num_kv_heads", i32),
                 ("head_dim", i32), ("block_size", i32), ("max_blocks_per_seq", i32),
                 ("num_blocks", i32), ("dtype", i32), ("max_context", i32), ("path", i32),
-                ("partition_tokens", i32), ("reserved", i32 * 5)]
+                ("partition_tokens", i32), ("waves_per_group", i32), ("reserved", i32 * 4)]
 
 
 class AttnPlan(C.Structure):
-    _fields_ = [("path", i32), ("partition_tokens", i32), ("num_partitions", i32),
+    _fields_ = [("path", i32), ("schedule", i32), ("partition_tokens", i32), ("num_partitions", i32),
                 ("waves_per_group", i32), ("grid", i32), ("merge_grid", i32),
                 ("workspace_bytes", sz)]
 

@@ -68,22 +68,35 @@ class PagedKVCache:
         return torch.from_numpy(self.tables).to(self.device)
 
     # -- attention --------------------------------------------------------
-    def desc(self, num_q_heads: int, max_context: int, path=_lib.PA_PATH_AUTO, partition_tokens=0):
+    def desc(self, num_q_heads: int, max_context: int, path=_lib.PA_PATH_AUTO, partition_tokens=0,
+             waves_per_group=0):
         return api.make_desc(self.tables.shape[0], num_q_heads, self.hkv, self.d, self.bs,
-                             self.tables.shape[1], self.nb, self.dtype, max_context, path, partition_tokens)
+                             self.tables.shape[1], self.nb, self.dtype, max_context, path, partition_tokens,
+                             waves_per_group)
 
     def attention(self, q, tables_dev, lens_dev, q_len: int, scale: float, max_context: int,
-                  path=_lib.PA_PATH_AUTO, partition_tokens=0, out=None, workspace=None, stream=None):
+                  path=_lib.PA_PATH_AUTO, partition_tokens=0, waves_per_group=0, out=None, workspace=None,
+                  stream=None):
         import torch
-        desc = self.desc(q.shape[2], max_context, path, partition_tokens)
+        desc = self.desc(q.shape[2], max_context, path, partition_tokens, waves_per_group)
         if out is None:
             out = torch.empty_like(q)
         need = api.pa_attention_workspace_size(desc, q_len)
         if workspace is None and need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = self.workspace(need, q.device)
         api.pa_attention(desc, q, self.k_pool, self.v_pool, tables_dev, lens_dev, q_len, scale, out,
                          workspace, stream)
         return out
+
+    def workspace(self, nbytes: int, device):
+        """A zero-filled workspace of at least nbytes, kept for later calls (its
+        arrival counters are left zero by every completed call)."""
+        import torch
+        ws = getattr(self, "_ws", None)
+        if ws is None or ws.numel() < nbytes or ws.device != torch.device(device):
+            ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+            self._ws = ws
+        return ws
 
     # -- a whole synthetic batch ---------------------------------------------
     @classmethod

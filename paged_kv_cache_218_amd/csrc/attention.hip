@@ -36,13 +36,14 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 
 #include "pa_internal.h"
 
 namespace {
 
 constexpr int kCUs = 256;              // MI355X compute units
-constexpr int kMaxPartitions = 4096;   // merge kernel keeps P weights in LDS
+constexpr int kMaxPartitions = 1 << 16;  // partitions per sequence
 constexpr int kMfmaMaxRows = 32;       // two 16-row tiles
 constexpr int kValuMaxRows = 16;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -61,9 +62,10 @@ struct AttnArgs {
   const int32_t* tables;
   const int32_t* lens;
   void* out;
-  float* part_ml;  // [rows_total][P][2]  (m in base-2 units, l)
-  float* part_o;   // [rows_total][P][d]
-  int32_t hq, hkv, group, mb, nb, q_len, max_ctx, parts, part_tokens;
+  float* part_ml;  // partitions: [rows_total][P][2]; balanced: [pieces][R][2] (m base-2, l)
+  float* part_o;   // partitions: [rows_total][P][d]; balanced: [pieces][R][d]
+  int32_t* counters;  // balanced: arrival count per segment, zero between calls
+  int32_t num_seqs, hq, hkv, group, mb, nb, q_len, max_ctx, parts, part_tokens;
   float scale_log2;  // scale * log2(e)
 };
 
@@ -91,6 +93,18 @@ template <> __device__ __forceinline__ void store_f<float>(float* p, float v) { 
 template <> __device__ __forceinline__ void store_f<uint16_t>(uint16_t* p, float v) { *p = f_to_bf16(v); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Device-coherent accesses for data handed between workgroups of one launch
+// (which may sit on different XCDs, each with its own L2): agent-scope
+// relaxed atomic stores write through to the device-coherent level and
+// agent-scope relaxed atomic loads read from it, so no L2 writeback or
+// invalidate is needed.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Decode the workgroup id. Returns false when the partition is empty.
 struct Tile {
@@ -138,7 +152,7 @@ __device__ void merge_and_store(const AttnArgs& a, const Tile& t, int R, int row
     }
     const float val = poisoned ? NAN : (l > 0.f ? o / l : 0.f);
     const int row = out_row(a, t.b, t.g, r);
-    if (a.parts == 1) {
+    if (t.L <= a.part_tokens) {  // the sequence has this one partition: final output
       store_f<T>(static_cast<T*>(a.out) + int64_t(row) * D + c, val);
     } else {
       const int64_t pi = int64_t(row) * a.parts + t.part;
@@ -163,7 +177,7 @@ __device__ void poison_rows(const AttnArgs& a, const Tile& t, int R) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel (bf16)
+// MFMA path (bf16)
 // ---------------------------------------------------------------------------
 // Lane l: n = l % 16 (query row within a 16-row tile), j = l / 16.
 // v_mfma_f32_16x16x32_bf16 operands: A lane l holds A[m = l%16][k = 8j..8j+7],
@@ -174,23 +188,54 @@ __device__ void poison_rows(const AttnArgs& a, const Tile& t, int R) {
 // PV: O^T[d][row] += V^T[d][tok] P^T[tok][row]; the B operand is the lane's
 //   own 8 probabilities (tokens 8j..8j+7 of row n), the A operand 8 adjacent
 //   tokens of one head-dim row of the V^T slice: 16 contiguous bytes.
-template <int D, int BS, int NT>
-__global__ __launch_bounds__(256) void mfma_attn(AttnArgs a) {
+constexpr int kStep = 32;  // tokens per MFMA step
+
+template <int D>
+struct StepBuf {
+  u32x4 k[2][D / 32];  // two 16-token K tiles, D/32 k-steps each
+  u32x4 v[D / 16];     // V^T head-dim tiles
+  int tb;              // first token of the step
+  bool ok;             // block ids in range
+};
+
+// Online-softmax state of one wavefront: lane (n, j) holds row 16*nt + n,
+// head-dim elements 16*dt + 4*j .. +3 of the accumulator.
+template <int D, int NT>
+struct WaveState {
+  f32x4 acc[NT][D / 16];
+  float m[NT], l[NT];
+  bool poisoned;
+};
+
+template <int D, int NT>
+__device__ __forceinline__ void wave_state_init(WaveState<D, NT>& st) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    st.m[nt] = -INFINITY;
+    st.l[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) st.acc[nt][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+  st.poisoned = false;
+}
+
+// One wavefront's share of a piece: steps first, first+W, ... < end of
+// sequence b (context L), KV head g. Every step covers 32 tokens; tokens at
+// or past L, and tokens after a row's causal limit, are masked.
+template <int D, int BS, int NT, bool PIPE>
+__device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int first, int end, int W,
+                                WaveState<D, NT>& st) {
   constexpr int KS = D / 32;  // k-steps over the head dim for QK
   constexpr int DT = D / 16;  // 16-row tiles of the head dim for PV
-  extern __shared__ float smem[];
-  const int W = blockDim.x / 64;
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int lane = threadIdx.x % 64;
   const int n = lane & 15, j = lane >> 4;
-  const Tile t = decode_tile(a);
   const int R = a.group * a.q_len;
-  if (t.bad) { poison_rows<uint16_t, D>(a, t, R); return; }
-  if (t.t0 >= t.L) return;
+  if (first >= end) return;
 
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(a.k_pool);
   const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v_pool);
-  const int32_t* __restrict__ table = a.tables + int64_t(t.b) * a.mb;
+  const int32_t* __restrict__ table = a.tables + int64_t(b) * a.mb;
 
   // query rows as the B operand of QK, per 16-row tile and k-step
   u32x4 qop[NT][KS];
@@ -198,99 +243,76 @@ __global__ __launch_bounds__(256) void mfma_attn(AttnArgs a) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = nt * 16 + n;
-    lim[nt] = t.L - a.q_len + min(r, R - 1) / a.group;
+    lim[nt] = L - a.q_len + min(r, R - 1) / a.group;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = {0, 0, 0, 0};
       if (r < R) {
-        const int i = r / a.group, h = t.g * a.group + r % a.group;
-        v = *reinterpret_cast<const u32x4*>(q + (int64_t(t.b * a.q_len + i) * a.hq + h) * D + 32 * ks + 8 * j);
+        const int i = r / a.group, h = g * a.group + r % a.group;
+        v = *reinterpret_cast<const u32x4*>(q + (int64_t(b * a.q_len + i) * a.hq + h) * D + 32 * ks + 8 * j);
       }
       qop[nt][ks] = v;
     }
   }
 
-  f32x4 acc[NT][DT];
-  float m_run[NT], l_run[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[nt][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  }
-  bool poisoned = false;
-
-  const int nsteps = (t.t1 - t.t0 + 31) / 32;
   const int64_t head_stride = int64_t(BS) * D;  // elements of one (block, head) slice
-  for (int s = wave; s < nsteps; s += W) {
-    const int tb = t.t0 + 32 * s;
-    // physical blocks of this step (uniform across the wave)
-    int blk0 = table[tb / BS];
-    int blk1 = blk0;
-    bool have1 = true;
-    if (BS == 16) {
-      have1 = tb + 16 < t.L;
-      blk1 = have1 ? table[tb / BS + 1] : blk0;
-    }
-    if (blk0 < 0 || blk0 >= a.nb || blk1 < 0 || blk1 >= a.nb) {
-      poisoned = true;
-      continue;
-    }
-    const uint16_t* kb0 = kp + (int64_t(blk0) * a.hkv + t.g) * head_stride;
-    const uint16_t* kb1 = kp + (int64_t(blk1) * a.hkv + t.g) * head_stride;
-    const uint16_t* vb0 = vp + (int64_t(blk0) * a.hkv + t.g) * head_stride;
-    const uint16_t* vb1 = vp + (int64_t(blk1) * a.hkv + t.g) * head_stride;
 
+  // Issue the loads of one 32-token step into a register buffer. The
+  // physical block ids are scalar (wave-uniform) loads from the table.
+  auto load_step = [&](StepBuf<D>& buf, int step) {
+    const int tb = kStep * step;
+    buf.tb = tb;
+    const int blk0 = table[tb / BS];
+    const bool have1 = BS == 32 || tb + 16 < L;
+    const int blk1 = (BS == 16 && have1) ? table[tb / BS + 1] : blk0;
+    buf.ok = blk0 >= 0 && blk0 < a.nb && blk1 >= 0 && blk1 < a.nb;
+    const int64_t o0 = buf.ok ? (int64_t(blk0) * a.hkv + g) * head_stride : 0;
+    const int64_t o1 = buf.ok ? (int64_t(blk1) * a.hkv + g) * head_stride : 0;
     // K tiles: A operand, token of row n in tile i
-    u32x4 kop[2][KS];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int tok = 8 * (n >> 2) + 4 * i + (n & 3);
-      const uint16_t* row;
-      bool ok = true;
-      if (BS == 32) {
-        row = kb0 + tok * D;
-      } else {
-        row = (tok < 16 ? kb0 : kb1) + (tok & 15) * D;
-        ok = tok < 16 || have1;
-      }
+      const bool second = BS == 16 && tok >= 16;
+      const uint16_t* row = kp + (second ? o1 : o0) + (tok & (BS - 1)) * D + 8 * j;
+      const bool ok = buf.ok && (!second || have1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4 v = {0, 0, 0, 0};
-        if (ok) v = *reinterpret_cast<const u32x4*>(row + 32 * ks + 8 * j);
-        kop[i][ks] = v;
+        if (ok) v = *reinterpret_cast<const u32x4*>(row + 32 * ks);
+        buf.k[i][ks] = v;
       }
     }
     // V^T slices: A operand of PV, head-dim row 16*dt + n, tokens 8j..8j+7
-    u32x4 vop[DT];
     {
-      const uint16_t* base;
-      bool ok = true;
-      if (BS == 32) {
-        base = vb0 + 8 * j;
-      } else {
-        base = (j < 2 ? vb0 : vb1) + 8 * (j & 1);
-        ok = j < 2 || have1;
-      }
+      const bool second = BS == 16 && j >= 2;
+      const uint16_t* base = vp + (second ? o1 : o0) + (BS == 32 ? 8 * j : 8 * (j & 1)) + n * BS;
+      const bool ok = buf.ok && (!second || have1);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         u32x4 v = {0, 0, 0, 0};
-        if (ok) v = *reinterpret_cast<const u32x4*>(base + (16 * dt + n) * BS);
-        vop[dt] = v;
+        if (ok) v = *reinterpret_cast<const u32x4*>(base + 16 * dt * BS);
+        buf.v[dt] = v;
       }
     }
+  };
+
+  // Scores, online softmax and P.V of one loaded step.
+  auto compute_step = [&](StepBuf<D>& buf) {
+    const int tb = buf.tb;
+    if (!buf.ok) {
+      st.poisoned = true;
+      return;
+    }
     // tail step: zero V entries past the context so 0 * NaN never reaches the sum
-    if (tb + 32 > t.L) {
-      const int valid = min(max(t.L - (tb + 8 * j), 0), 8);  // tokens of this lane's 8 still valid
+    if (tb + kStep > L) {
+      const int valid = min(max(L - (tb + 8 * j), 0), 8);  // tokens of this lane's 8 still valid
 #pragma unroll
       for (int w4 = 0; w4 < 4; ++w4) {
         const uint32_t keep = (2 * w4 + 1 < valid) ? 0xffffffffu : (2 * w4 < valid ? 0x0000ffffu : 0u);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vop[dt][w4] &= keep;
+        for (int dt = 0; dt < DT; ++dt) buf.v[dt][w4] &= keep;
       }
     }
-
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f32x4 sc[2];
@@ -299,7 +321,7 @@ __global__ __launch_bounds__(256) void mfma_attn(AttnArgs a) {
         sc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          sc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[i][ks]),
+          sc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf.k[i][ks]),
                                                            __builtin_bit_cast(bf16x8, qop[nt][ks]),
                                                            sc[i], 0, 0, 0);
       }
@@ -311,17 +333,17 @@ __global__ __launch_bounds__(256) void mfma_attn(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int tok = tb + 8 * j + 4 * i + r;
-          const bool vis = tok < t.t1 && tok <= lim[nt];
+          const bool vis = tok < L && tok <= lim[nt];
           const float v = vis ? sc[i][r] * a.scale_log2 : -INFINITY;
           s2[4 * i + r] = v;
           mx = fmaxf(mx, v);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[nt], mx);
+      const float m_new = fmaxf(st.m[nt], mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[nt] - m_use);
-      m_run[nt] = m_new;
+      const float alpha = fast_exp2(st.m[nt] - m_use);
+      st.m[nt] = m_new;
       uint32_t pk[4];
       float psum = 0.f;
 #pragma unroll
@@ -333,26 +355,56 @@ __global__ __launch_bounds__(256) void mfma_attn(AttnArgs a) {
         // the sum uses the rounded weights, so the output stays a convex combination
         psum += __uint_as_float(packed << 16) + __uint_as_float(packed & 0xffff0000u);
       }
-      l_run[nt] = l_run[nt] * alpha + psum;
+      st.l[nt] = st.l[nt] * alpha + psum;
       const u32x4 pop = {pk[0], pk[1], pk[2], pk[3]};
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        acc[nt][dt] *= alpha;
-        acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[dt]),
-                                                              __builtin_bit_cast(bf16x8, pop),
-                                                              acc[nt][dt], 0, 0, 0);
+        st.acc[nt][dt] *= alpha;
+        st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf.v[dt]),
+                                                                 __builtin_bit_cast(bf16x8, pop),
+                                                                 st.acc[nt][dt], 0, 0, 0);
       }
     }
-  }
+  };
 
-  // row sums: each lane holds its 8-token share; add the 4 lanes of the row
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    l_run[nt] += __shfl_xor(l_run[nt], 16);
-    l_run[nt] += __shfl_xor(l_run[nt], 32);
+  if constexpr (PIPE) {
+    // Ping-pong over two register buffers: the loads of the wave's next step
+    // are in flight while the current step is computed.
+    StepBuf<D> bufA, bufB;
+    int s = first;
+    load_step(bufA, s);
+    while (s < end) {
+      if (s + W < end) load_step(bufB, s + W);
+      compute_step(bufA);
+      s += W;
+      if (s >= end) break;
+      if (s + W < end) load_step(bufA, s + W);
+      compute_step(bufB);
+      s += W;
+    }
+  } else {
+    // one buffer: other waves on the SIMD hide this wave's load latency
+    StepBuf<D> buf;
+    for (int s = first; s < end; s += W) {
+      load_step(buf, s);
+      compute_step(buf);
+    }
   }
-  // park the per-wave states of the R real rows in LDS:
-  // m_s[W][R], l_s[W][R], o_s[W][R][D]
+}
+
+// Park each wave's state of the R real rows in LDS (m_s[W][R], l_s[W][R],
+// o_s[W][R][D]) and return whether any wave of the workgroup saw a bad block.
+template <int D, int NT>
+__device__ bool park_states(const WaveState<D, NT>& st, int R, float* smem) {
+  const int W = blockDim.x / 64;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int n = lane & 15, j = lane >> 4;
+  float l_row[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {  // row sums: add the 4 lanes of the row
+    l_row[nt] = st.l[nt] + __shfl_xor(st.l[nt], 16);
+    l_row[nt] += __shfl_xor(l_row[nt], 32);
+  }
   float* m_s = smem;
   float* l_s = m_s + W * R;
   float* o_s = l_s + W * R;
@@ -361,18 +413,228 @@ __global__ __launch_bounds__(256) void mfma_attn(AttnArgs a) {
     const int r = nt * 16 + n;
     if (r < R) {
       if (j == 0) {
-        m_s[wave * R + r] = m_run[nt];
-        l_s[wave * R + r] = l_run[nt];
+        m_s[wave * R + r] = st.m[nt];
+        l_s[wave * R + r] = l_row[nt];
       }
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o_s[(wave * R + r) * D + 16 * dt + 4 * j + k] = acc[nt][dt][k];
+        for (int k = 0; k < 4; ++k) o_s[(wave * R + r) * D + 16 * dt + 4 * j + k] = st.acc[nt][dt][k];
     }
   }
-  // a bad table entry in any wave poisons the whole workgroup
-  const int any_bad = __syncthreads_or(poisoned ? 1 : 0);
-  merge_and_store<uint16_t, D>(a, t, R, R, W, m_s, l_s, o_s, any_bad != 0);
+  return __syncthreads_or(st.poisoned ? 1 : 0) != 0;
+}
+
+// Combine the W parked states of row r, column c: (M, l, o/l).
+__device__ __forceinline__ void combine_waves(const float* smem, int W, int R, int D, int r, int c,
+                                              float& M, float& l, float& o) {
+  const float* m_s = smem;
+  const float* l_s = m_s + W * R;
+  const float* o_s = l_s + W * R;
+  M = -INFINITY;
+  for (int w = 0; w < W; ++w) M = fmaxf(M, m_s[w * R + r]);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  l = 0.f;
+  float acc = 0.f;
+  for (int w = 0; w < W; ++w) {
+    const float f = fast_exp2(m_s[w * R + r] - Mu);
+    l += f * l_s[w * R + r];
+    acc += f * o_s[(w * R + r) * D + c];
+  }
+  o = l > 0.f ? acc / l : 0.f;
+}
+
+// Fixed partitions: workgroup = (sequence, KV head, partition); partitions
+// that do not cover the whole sequence leave partials for lse_merge.
+template <int D, int BS, int NT, bool PIPE>
+__global__ __launch_bounds__(256, 2) void mfma_attn(AttnArgs a) {
+  extern __shared__ float smem[];
+  const int W = blockDim.x / 64, wave = threadIdx.x / 64;
+  const Tile t = decode_tile(a);
+  const int R = a.group * a.q_len;
+  if (t.bad) { poison_rows<uint16_t, D>(a, t, R); return; }
+  if (t.t0 >= t.L) return;
+  WaveState<D, NT> st;
+  wave_state_init(st);
+  const int s0 = t.t0 / kStep, s1 = (t.t1 + kStep - 1) / kStep;
+  mfma_wave_steps<D, BS, NT, PIPE>(a, t.b, t.g, t.L, s0 + wave, s1, W, st);
+  const bool bad = park_states(st, R, smem);
+  merge_and_store<uint16_t, D>(a, t, R, R, W, smem, smem + W * R, smem + 2 * W * R, bad);
+}
+
+// Balanced schedule. The work of the batch is the list of segments
+// s = b * H_kv + g, each ceil(L_b / 32) steps long, laid end to end; the grid
+// (sized to the resident capacity) splits that list into equal contiguous
+// ranges, one per workgroup. The part of a segment inside one workgroup's
+// range is a piece; a segment covered by one piece is written directly,
+// otherwise every piece writes (m, l, o) partials at index
+// (workgroup + segment) and the workgroup that completes a segment's last
+// piece, by an atomic arrival count per segment, merges them.
+__device__ __forceinline__ int64_t range_start(int64_t k, int64_t S, int64_t N) { return k * S / N; }
+
+// workgroup whose range contains position x (0 <= x < S)
+__device__ __forceinline__ int64_t owner(int64_t x, int64_t S, int64_t N) {
+  int64_t k = x * N / S;
+  while (k + 1 < N && range_start(k + 1, S, N) <= x) ++k;
+  while (k > 0 && range_start(k, S, N) > x) --k;
+  return k;
+}
+
+template <int D, int BS, int NT, bool PIPE>
+__global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
+  extern __shared__ float smem[];  // [B+1] step prefix sums, then the parked states
+  const int W = blockDim.x / 64, wave = threadIdx.x / 64;
+  const int R = a.group * a.q_len;
+  const int B = a.num_seqs;
+  int32_t* pre = reinterpret_cast<int32_t*>(smem);
+  float* park = smem + ((B + 1 + 3) & ~3);
+  // steps per sequence (0 for an out-of-range length) and their prefix sums:
+  // thread t owns a contiguous chunk of sequences; chunk totals are scanned
+  // across the workgroup with wave shuffles and per-wave totals in LDS
+  {
+    const int T = blockDim.x, tid = threadIdx.x;
+    const int chunk = (B + T - 1) / T;
+    const int b0 = min(B, tid * chunk), b1 = min(B, b0 + chunk);
+    auto steps_of = [&](int b) {
+      const int L = a.lens[b];
+      return (L < a.q_len || L > a.max_ctx) ? 0 : (L + kStep - 1) / kStep;
+    };
+    int local = 0;
+    for (int b = b0; b < b1; ++b) local += steps_of(b);
+    int incl = local;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if ((tid & 63) >= o) incl += v;
+    }
+    __shared__ int wave_tot[4];
+    if ((tid & 63) == 63) wave_tot[tid >> 6] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < (tid >> 6); ++w) run += wave_tot[w];
+    for (int b = b0; b < b1; ++b) {
+      pre[b] = run;
+      run += steps_of(b);
+    }
+    if (b1 == B && b0 < b1) pre[B] = run;
+    if (B <= tid * chunk && tid == 0) pre[B] = 0;
+    __syncthreads();
+  }
+  const int64_t k = blockIdx.x;
+  const int64_t S = int64_t(pre[B]) * a.hkv;
+  // sequences with an out-of-range length: NaN rows, spread over the grid
+  for (int b = int(k); b < B; b += int(gridDim.x)) {
+    const int L = a.lens[b];
+    if (L < a.q_len || L > a.max_ctx)
+      for (int e = threadIdx.x; e < a.q_len * a.hq * D; e += blockDim.x)
+        store_f<uint16_t>(static_cast<uint16_t*>(a.out) + int64_t(b) * a.q_len * a.hq * D + e, NAN);
+  }
+  // With no more workgroups than steps every range is non-empty, so the
+  // pieces of a segment are exactly the workgroups from its first owner to
+  // its last.
+  const int64_t N = min(int64_t(gridDim.x), S);
+  if (k >= N) return;
+  const int64_t x0 = range_start(k, S, N), x1 = range_start(k + 1, S, N);
+  // first sequence whose segments reach past x0
+  int b = 0;
+  {
+    int lo = 0, hi = B - 1;  // largest b with hkv * pre[b] <= x0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (int64_t(pre[mid]) * a.hkv <= x0) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  }
+  int64_t x = x0;
+  while (x < x1) {
+    int nb = pre[b + 1] - pre[b];
+    if (nb == 0 || int64_t(pre[b + 1]) * a.hkv <= x) { ++b; continue; }
+    const int64_t seq_start = int64_t(pre[b]) * a.hkv;
+    const int g = int((x - seq_start) / nb);
+    const int64_t seg_start = seq_start + int64_t(g) * nb, seg_end = seg_start + nb;
+    const int first = int(x - seg_start), last = int(min(x1, seg_end) - seg_start);
+    const int L = a.lens[b];
+    WaveState<D, NT> st;
+    wave_state_init(st);
+    mfma_wave_steps<D, BS, NT, PIPE>(a, b, g, L, first + wave, last, W, st);
+    const bool bad = park_states(st, R, park);
+    const int64_t seg = int64_t(b) * a.hkv + g;
+    const bool whole = first == 0 && last == nb;
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+    if (whole) {
+      for (int e = threadIdx.x; e < R * D; e += blockDim.x) {
+        const int r = e / D, c = e % D;
+        float M, l, o;
+        combine_waves(park, W, R, D, r, c, M, l, o);
+        store_f<uint16_t>(out + int64_t(out_row(a, b, g, r)) * D + c, bad ? NAN : o);
+      }
+    } else {
+      const int64_t piece = k + seg;
+      for (int e = threadIdx.x; e < R * D; e += blockDim.x) {
+        const int r = e / D, c = e % D;
+        float M, l, o;
+        combine_waves(park, W, R, D, r, c, M, l, o);
+        store_coherent(&a.part_o[(piece * R + r) * D + c], bad ? NAN : o);
+        if (c == 0) {
+          store_coherent(&a.part_ml[(piece * R + r) * 2 + 0], bad ? NAN : M);
+          store_coherent(&a.part_ml[(piece * R + r) * 2 + 1], bad ? NAN : l);
+        }
+      }
+      // Every wave waits until its partial stores are complete at the
+      // coherent level, then one thread counts the piece in. The workgroup
+      // that brings the count to the number of pieces read the others'
+      // partials after seeing their increments, and merges.
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const int64_t k_first = owner(seg_start, S, N), k_last = owner(seg_end - 1, S, N);
+      const int npieces = int(k_last - k_first + 1);
+      __shared__ int arrived;
+      if (threadIdx.x == 0)
+        arrived = __hip_atomic_fetch_add(&a.counters[seg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (arrived == npieces - 1) {
+        const int64_t p0 = k_first + seg;
+        // per row: global maximum and weight sum (rows spread over the threads)
+        __shared__ float row_M[kMfmaMaxRows], row_den[kMfmaMaxRows];
+        for (int r = threadIdx.x; r < R; r += blockDim.x) {
+          float M = -INFINITY;
+          for (int p = 0; p < npieces; ++p) M = fmaxf(M, load_coherent(&a.part_ml[((p0 + p) * R + r) * 2]));
+          const float Mu = (M == -INFINITY) ? 0.f : M;
+          float den = 0.f;
+          for (int p = 0; p < npieces; ++p) {
+            const int64_t pr = (p0 + p) * R + r;
+            den += load_coherent(&a.part_ml[pr * 2 + 1]) * fast_exp2(load_coherent(&a.part_ml[pr * 2]) - Mu);
+          }
+          row_M[r] = Mu;
+          row_den[r] = den;
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < R * D; e += blockDim.x) {
+          const int r = e / D, c = e % D;
+          const float Mu = row_M[r];
+          float num0 = 0.f, num1 = 0.f;
+          int p = 0;
+          for (; p + 1 < npieces; p += 2) {
+            const int64_t pr0 = (p0 + p) * R + r, pr1 = pr0 + R;
+            const float w0 = load_coherent(&a.part_ml[pr0 * 2 + 1]) * fast_exp2(load_coherent(&a.part_ml[pr0 * 2]) - Mu);
+            const float w1 = load_coherent(&a.part_ml[pr1 * 2 + 1]) * fast_exp2(load_coherent(&a.part_ml[pr1 * 2]) - Mu);
+            num0 = fmaf(w0, load_coherent(&a.part_o[pr0 * D + c]), num0);
+            num1 = fmaf(w1, load_coherent(&a.part_o[pr1 * D + c]), num1);
+          }
+          if (p < npieces) {
+            const int64_t pr = (p0 + p) * R + r;
+            num0 = fmaf(load_coherent(&a.part_ml[pr * 2 + 1]) * fast_exp2(load_coherent(&a.part_ml[pr * 2]) - Mu),
+                        load_coherent(&a.part_o[pr * D + c]), num0);
+          }
+          const float den = row_den[r];
+          store_f<uint16_t>(out + int64_t(out_row(a, b, g, r)) * D + c, den > 0.f ? (num0 + num1) / den : NAN);
+        }
+        if (threadIdx.x == 0)  // ready for the next call
+          __hip_atomic_store(&a.counters[seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();  // the park area is reused by the next piece
+    x = seg_start + last;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -551,64 +813,101 @@ __global__ __launch_bounds__(256) void valu_attn(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of partition partials
 // ---------------------------------------------------------------------------
-// One workgroup (D threads) per output row: M = max_p m_p, w_p = l_p 2^(m_p-M),
-// out = sum_p w_p o_p / sum_p w_p over the partitions the sequence has.
+// One workgroup of kMergeWaves wavefronts per output row of a sequence that
+// has more than one partition: M = max_p m_p, w_p = l_p 2^(m_p - M),
+// out = sum_p w_p o_p / sum_p w_p. Wave w takes partitions w, w+4, ...; each
+// lane holds D/64 head-dim elements; the waves' sums meet in LDS.
+constexpr int kMergeWaves = 4;
+
 template <typename T, int D>
-__global__ __launch_bounds__(128) void lse_merge(AttnArgs a) {
-  __shared__ float w_s[kMaxPartitions];
-  __shared__ float red[D / 64 + 1];
+__global__ __launch_bounds__(256) void lse_merge(AttnArgs a) {
+  constexpr int DPL = D / 64;
+  __shared__ float red_m[kMergeWaves];
+  __shared__ float red_o[kMergeWaves][D + 1];
   const int row = blockIdx.x;
   const int b = row / (a.q_len * a.hq);
   const int L = a.lens[b];
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   T* out = static_cast<T*>(a.out) + int64_t(row) * D;
-  const int c = threadIdx.x;
   if (L < a.q_len || L > a.max_ctx) {
-    store_f<T>(out + c, NAN);
+    for (int c = threadIdx.x; c < D; c += blockDim.x) store_f<T>(out + c, NAN);
     return;
   }
   const int np = (L + a.part_tokens - 1) / a.part_tokens;
+  if (np == 1) return;  // written by the partition kernel
   const float* ml = a.part_ml + int64_t(row) * a.parts * 2;
   const float* po = a.part_o + int64_t(row) * a.parts * D;
-  // global maximum
+  // global maximum over the partitions
   float mx = -INFINITY;
-  for (int p = c; p < np; p += D) mx = fmaxf(mx, ml[2 * p]);
+  for (int p = threadIdx.x; p < np; p += blockDim.x) mx = fmaxf(mx, ml[2 * p]);
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  if ((c & 63) == 0) red[c / 64] = mx;
+  if (lane == 0) red_m[wave] = mx;
   __syncthreads();
-  float M = red[0];
-  for (int k = 1; k < D / 64; ++k) M = fmaxf(M, red[k]);
-  __syncthreads();
+  float M = red_m[0];
+  for (int w = 1; w < kMergeWaves; ++w) M = fmaxf(M, red_m[w]);
   const float Mu = (M == -INFINITY) ? 0.f : M;
-  float wsum = 0.f;
-  for (int p = c; p < np; p += D) {
-    const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - Mu);
-    w_s[p] = w;
-    wsum += w;
+  // weighted sums; four partitions in flight per wave
+  float acc[DPL], wsum = 0.f;
+  for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+  int p = wave;
+  for (; p + 3 * kMergeWaves < np; p += 4 * kMergeWaves) {
+    float w4[4], o4[4][DPL];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pu = p + u * kMergeWaves;
+      w4[u] = ml[2 * pu + 1] * fast_exp2(ml[2 * pu] - Mu);
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) o4[u][k] = po[int64_t(pu) * D + lane + 64 * k];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      wsum += w4[u];
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) acc[k] = fmaf(w4[u], o4[u][k], acc[k]);
+    }
   }
-  for (int o = 32; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o);
-  if ((c & 63) == 0) red[c / 64] = wsum;
+  for (; p < np; p += kMergeWaves) {
+    const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - Mu);
+    wsum += w;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[k] = fmaf(w, po[int64_t(p) * D + lane + 64 * k], acc[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) red_o[wave][lane + 64 * k] = acc[k];
+  if (lane == 0) red_o[wave][D] = wsum;
   __syncthreads();
-  float denom = 0.f;
-  for (int k = 0; k < D / 64; ++k) denom += red[k];
-  float acc = 0.f;
-  for (int p = 0; p < np; ++p) acc = fmaf(w_s[p], po[int64_t(p) * D + c], acc);
-  store_f<T>(out + c, denom > 0.f ? acc / denom : NAN);
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float num = 0.f, den = 0.f;
+    for (int w = 0; w < kMergeWaves; ++w) {
+      num += red_o[w][c];
+      den += red_o[w][D];
+    }
+    store_f<T>(out + c, den > 0.f ? num / den : NAN);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Host side: validation, planning, launch
 // ---------------------------------------------------------------------------
 struct Plan {
-  int path, part_tokens, parts, waves, grid, merge_grid, nt, rows;
+  int path, sched, part_tokens, parts, waves, grid, merge_grid, nt, rows;
+  bool pipe;
+  int64_t segments, pieces;  // balanced schedule: segments, partial slots
   size_t ws;
 };
 
+constexpr int kMaxBalancedSeqs = 8192;  // step prefix sums live in LDS
+
 int ceil_div(int64_t x, int64_t y) { return int((x + y - 1) / y); }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   if (!d || !pl) return PA_ERR_INVALID_ARG;
-  for (int k = 0; k < 5; ++k)
+  for (int k = 0; k < 4; ++k)
     if (d->reserved[k] != 0) return PA_ERR_INVALID_ARG;
+  if (d->waves_per_group != 0 && d->waves_per_group != 1 && d->waves_per_group != 2 &&
+      d->waves_per_group != 4)
+    return PA_ERR_INVALID_ARG;
   if (d->num_seqs < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
       d->num_q_heads % d->num_kv_heads != 0 || d->max_blocks_per_seq < 1 || d->num_blocks < 1 ||
       q_len < 1 || d->max_context < 1 || d->partition_tokens < 0 || d->partition_tokens % 64 != 0)
@@ -633,8 +932,34 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   } else {
     return PA_ERR_INVALID_ARG;
   }
-  const int waves = 4;
+  const int waves = d->waves_per_group ? d->waves_per_group : 4;
   const int64_t pairs = int64_t(d->num_seqs) * d->num_kv_heads;
+  const int64_t out_rows = int64_t(d->num_seqs) * q_len * d->num_q_heads;
+  if (out_rows > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  pl->path = path;
+  pl->waves = waves;
+  pl->nt = rows > 16 ? 2 : 1;
+  pl->rows = int(rows);
+  pl->pipe = pl->nt == 1;
+  if (const char* e = getenv("PA_EXP_PIPE")) pl->pipe = e[0] == '1';
+  const bool balanced = path == PA_PATH_MFMA && d->partition_tokens == 0 &&
+                        d->num_seqs <= kMaxBalancedSeqs;
+  if (balanced) {
+    // grid = resident capacity; the workspace is sized for the largest one
+    // (every compute unit full of single-workgroup waves)
+    const int64_t grid_max = int64_t(kCUs) * (32 / waves);
+    pl->sched = PA_SCHED_BALANCED;
+    pl->part_tokens = 0;
+    pl->parts = 0;
+    pl->grid = int(grid_max);
+    pl->merge_grid = 0;
+    pl->segments = pairs;
+    pl->pieces = grid_max + pairs;
+    pl->ws = align256(size_t(pairs) * sizeof(int32_t)) +
+             align256(size_t(pl->pieces) * rows * 2 * sizeof(float)) +
+             size_t(pl->pieces) * rows * d->head_dim * sizeof(float);
+    return PA_OK;
+  }
   int pt = d->partition_tokens;
   if (pt == 0) {
     // enough waves to give every compute unit 8 of them, partitions >= 256 tokens
@@ -646,48 +971,80 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   const int parts = ceil_div(d->max_context, pt);
   if (parts > kMaxPartitions) return PA_ERR_UNSUPPORTED;
   const int64_t grid = pairs * parts;
-  const int64_t out_rows = int64_t(d->num_seqs) * q_len * d->num_q_heads;
-  if (grid > INT32_MAX || out_rows > INT32_MAX) return PA_ERR_UNSUPPORTED;
-  pl->path = path;
+  if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  pl->sched = PA_SCHED_PARTITIONS;
   pl->part_tokens = pt;
   pl->parts = parts;
-  pl->waves = waves;
   pl->grid = int(grid);
   pl->merge_grid = parts > 1 ? int(out_rows) : 0;
-  pl->nt = rows > 16 ? 2 : 1;
-  pl->rows = int(rows);
+  pl->segments = 0;
+  pl->pieces = 0;
   pl->ws = parts > 1 ? size_t(out_rows) * parts * (d->head_dim + 2) * sizeof(float) : 0;
   return PA_OK;
 }
 
-size_t lds_bytes(const Plan& pl, int D) {
-  if (pl.path == PA_PATH_MFMA) return size_t(pl.waves) * pl.rows * (D + 2) * sizeof(float);
+size_t lds_bytes(const Plan& pl, int D, int num_seqs) {
+  if (pl.path == PA_PATH_MFMA) {
+    const size_t park = size_t(pl.waves) * pl.rows * (D + 2) * sizeof(float);
+    if (pl.sched == PA_SCHED_PARTITIONS) return park;
+    return size_t((num_seqs + 1 + 3) & ~3) * sizeof(int32_t) + park;
+  }
   const size_t first = size_t(kValuMaxRows) * D + size_t(pl.waves) * kValuMaxRows * 64;
   const size_t merge = size_t(pl.waves) * kValuMaxRows * (D + 2);
   return std::max(first, merge) * sizeof(float);
 }
 
-template <int D, int BS>
-pa_status launch_main(const Plan& pl, int dtype, const AttnArgs& args, hipStream_t s) {
-  const dim3 grid(pl.grid), block(64 * pl.waves);
-  const size_t lds = lds_bytes(pl, D);
-  if (pl.path == PA_PATH_MFMA) {
-    if (pl.nt == 1) hipLaunchKernelGGL((mfma_attn<D, BS, 1>), grid, block, lds, s, args);
-    else hipLaunchKernelGGL((mfma_attn<D, BS, 2>), grid, block, lds, s, args);
-  } else if (dtype == PA_DTYPE_F32) {
-    hipLaunchKernelGGL((valu_attn<float, D, BS>), grid, block, lds, s, args);
-  } else {
-    hipLaunchKernelGGL((valu_attn<uint16_t, D, BS>), grid, block, lds, s, args);
+// Workgroups of `kernel` that fit on the device at once (0 if unknown).
+int resident_groups(const void* kernel, int threads, size_t lds) {
+  int per_cu = 0, dev = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess ||
+      hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
   }
+  return per_cu * cus;
+}
+
+template <typename K>
+pa_status launch(K kernel, const Plan& pl, size_t lds, const AttnArgs& args, hipStream_t s) {
+  int grid = pl.grid;
+  if (pl.sched == PA_SCHED_BALANCED) {
+    const int fit = resident_groups(reinterpret_cast<const void*>(kernel), 64 * pl.waves, lds);
+    grid = std::max(1, std::min(grid, fit > 0 ? fit : grid));
+  }
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * pl.waves), lds, s, args);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+template <int D, int BS>
+pa_status launch_main(const Plan& pl, int dtype, int num_seqs, const AttnArgs& args, hipStream_t s) {
+  const size_t lds = lds_bytes(pl, D, num_seqs);
+  if (pl.path == PA_PATH_MFMA && pl.sched == PA_SCHED_BALANCED) {
+    if (pl.nt == 1)
+      return pl.pipe ? launch(mfma_attn_balanced<D, BS, 1, true>, pl, lds, args, s)
+                     : launch(mfma_attn_balanced<D, BS, 1, false>, pl, lds, args, s);
+    return pl.pipe ? launch(mfma_attn_balanced<D, BS, 2, true>, pl, lds, args, s)
+                   : launch(mfma_attn_balanced<D, BS, 2, false>, pl, lds, args, s);
+  }
+  if (pl.path == PA_PATH_MFMA) {
+    if (pl.nt == 1)
+      return pl.pipe ? launch(mfma_attn<D, BS, 1, true>, pl, lds, args, s)
+                     : launch(mfma_attn<D, BS, 1, false>, pl, lds, args, s);
+    return pl.pipe ? launch(mfma_attn<D, BS, 2, true>, pl, lds, args, s)
+                   : launch(mfma_attn<D, BS, 2, false>, pl, lds, args, s);
+  }
+  if (dtype == PA_DTYPE_F32) return launch(valu_attn<float, D, BS>, pl, lds, args, s);
+  return launch(valu_attn<uint16_t, D, BS>, pl, lds, args, s);
 }
 
 template <int D>
 pa_status launch_merge(const Plan& pl, int dtype, const AttnArgs& args, hipStream_t s) {
+  const dim3 block(64 * kMergeWaves);
   if (dtype == PA_DTYPE_F32)
-    hipLaunchKernelGGL((lse_merge<float, D>), dim3(pl.merge_grid), dim3(D), 0, s, args);
+    hipLaunchKernelGGL((lse_merge<float, D>), dim3(pl.merge_grid), block, 0, s, args);
   else
-    hipLaunchKernelGGL((lse_merge<uint16_t, D>), dim3(pl.merge_grid), dim3(D), 0, s, args);
+    hipLaunchKernelGGL((lse_merge<uint16_t, D>), dim3(pl.merge_grid), block, 0, s, args);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -699,6 +1056,7 @@ extern "C" pa_status pa_attention_plan(const pa_attn_desc* desc, int32_t q_len, 
   pa_status st = make_plan(desc, q_len, &pl);
   if (st != PA_OK) return st;
   out->path = pl.path;
+  out->schedule = pl.sched;
   out->partition_tokens = pl.part_tokens;
   out->num_partitions = pl.parts;
   out->waves_per_group = pl.waves;
@@ -732,9 +1090,22 @@ extern "C" pa_status pa_attention(const pa_attn_desc* desc, const void* q, const
   args.tables = block_tables;
   args.lens = context_lens;
   args.out = out;
-  const int64_t out_rows = int64_t(desc->num_seqs) * q_len * desc->num_q_heads;
-  args.part_ml = pl.ws ? static_cast<float*>(workspace) : nullptr;
-  args.part_o = pl.ws ? static_cast<float*>(workspace) + out_rows * pl.parts * 2 : nullptr;
+  args.counters = nullptr;
+  args.part_ml = nullptr;
+  args.part_o = nullptr;
+  if (pl.sched == PA_SCHED_BALANCED) {
+    char* w = static_cast<char*>(workspace);
+    args.counters = reinterpret_cast<int32_t*>(w);
+    w += align256(size_t(pl.segments) * sizeof(int32_t));
+    args.part_ml = reinterpret_cast<float*>(w);
+    w += align256(size_t(pl.pieces) * pl.rows * 2 * sizeof(float));
+    args.part_o = reinterpret_cast<float*>(w);
+  } else if (pl.ws) {
+    const int64_t out_rows = int64_t(desc->num_seqs) * q_len * desc->num_q_heads;
+    args.part_ml = static_cast<float*>(workspace);
+    args.part_o = static_cast<float*>(workspace) + out_rows * pl.parts * 2;
+  }
+  args.num_seqs = desc->num_seqs;
   args.hq = desc->num_q_heads;
   args.hkv = desc->num_kv_heads;
   args.group = desc->num_q_heads / desc->num_kv_heads;
@@ -746,9 +1117,11 @@ extern "C" pa_status pa_attention(const pa_attn_desc* desc, const void* q, const
   args.part_tokens = pl.part_tokens;
   args.scale_log2 = scale * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int D = desc->head_dim, BS = desc->block_size;
-  if (D == 64) st = BS == 16 ? launch_main<64, 16>(pl, desc->dtype, args, s) : launch_main<64, 32>(pl, desc->dtype, args, s);
-  else st = BS == 16 ? launch_main<128, 16>(pl, desc->dtype, args, s) : launch_main<128, 32>(pl, desc->dtype, args, s);
-  if (st != PA_OK || pl.parts == 1) return st;
+  const int D = desc->head_dim, BS = desc->block_size, B = desc->num_seqs;
+  if (D == 64)
+    st = BS == 16 ? launch_main<64, 16>(pl, desc->dtype, B, args, s) : launch_main<64, 32>(pl, desc->dtype, B, args, s);
+  else
+    st = BS == 16 ? launch_main<128, 16>(pl, desc->dtype, B, args, s) : launch_main<128, 32>(pl, desc->dtype, B, args, s);
+  if (st != PA_OK || pl.merge_grid == 0) return st;
   return D == 64 ? launch_merge<64>(pl, desc->dtype, args, s) : launch_merge<128>(pl, desc->dtype, args, s);
 }

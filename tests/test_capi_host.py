@@ -203,7 +203,12 @@ def test_attention_plan_validation():
     ok = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
               max_blocks_per_seq=8, num_blocks=32, dtype=pa.PA_DTYPE_BF16, max_context=128)
     pl = pa.pa_attention_plan(pa.make_desc(**ok), 1)
-    assert pl.path == pa.PA_PATH_MFMA and pl.num_partitions >= 1
+    assert pl.path == pa.PA_PATH_MFMA and pl.schedule == _lib.PA_SCHED_BALANCED
+    assert pl.workspace_bytes == pa.pa_attention_workspace_size(pa.make_desc(**ok), 1) > 0
+    pl = pa.pa_attention_plan(pa.make_desc(**{**ok, "partition_tokens": 64}), 1)
+    assert pl.schedule == _lib.PA_SCHED_PARTITIONS and pl.num_partitions == 2
+    pl = pa.pa_attention_plan(pa.make_desc(**{**ok, "path": pa.PA_PATH_VALU}), 1)
+    assert pl.schedule == _lib.PA_SCHED_PARTITIONS
     bad = [
         (dict(num_q_heads=7), 1, _lib.PA_ERR_INVALID_ARG),
         (dict(head_dim=96), 1, _lib.PA_ERR_UNSUPPORTED),
@@ -215,6 +220,8 @@ def test_attention_plan_validation():
         (dict(dtype=7), 1, _lib.PA_ERR_UNSUPPORTED),
         (dict(num_q_heads=80, num_kv_heads=2), 1, _lib.PA_ERR_UNSUPPORTED),   # 40 rows
         (dict(dtype=pa.PA_DTYPE_F32, path=pa.PA_PATH_MFMA), 1, _lib.PA_ERR_UNSUPPORTED),
+        (dict(waves_per_group=3), 1, _lib.PA_ERR_INVALID_ARG),
+        (dict(waves_per_group=8), 1, _lib.PA_ERR_INVALID_ARG),
     ]
     for over, q_len, status in bad:
         with pytest.raises(pa.PAError) as e:

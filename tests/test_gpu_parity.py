@@ -49,6 +49,47 @@ def test_parity_small(key, path, part):
     assert_close(out_to_f64(out, w.cfg.dtype), ref, w.cfg.dtype, key)
 
 
+WAVE_CASES = [(k, wv) for k in ("8b", "70b", "verify", "long") for wv in (1, 2)]
+
+
+@pytest.mark.parametrize("key,waves", WAVE_CASES, ids=[f"{k}-w{wv}" for k, wv in WAVE_CASES])
+def test_parity_balanced_waves(key, waves):
+    """The balanced schedule with 1 or 2 wavefronts per workgroup (grid and
+    split points change with them)."""
+    w, ref = small(key)
+    out, _ = run_gpu(w, path=MFMA, waves=waves)
+    assert_close(out_to_f64(out, w.cfg.dtype), ref, w.cfg.dtype, f"{key} waves {waves}")
+
+
+@pytest.mark.parametrize("key", ["long", "8b", "verify"])
+def test_balanced_repeat_calls_reuse_workspace(key):
+    """Arrival counters are left zero, so repeated calls on one workspace give
+    identical bits (a piece merged before all partials were visible would
+    show up as a differing repeat)."""
+    import paged_kv_cache_218_amd as pa
+    w, ref = small(key)
+    cfg = w.cfg
+    out, cache = run_gpu(w, path=MFMA)
+    desc = cache.desc(cfg.num_q_heads, int(w.lens.max()), MFMA, 0, 0)
+    plan = pa.pa_attention_plan(desc, cfg.q_len)
+    assert plan.schedule == pa.PA_SCHED_BALANCED
+    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    first = None
+    for _ in range(8):
+        o = torch.empty_like(out)
+        q = torch.from_numpy(np.ascontiguousarray(w.q_all()).view(np.int16)).view(torch.bfloat16).cuda()
+        pa.pa_attention(desc, q, cache.k_pool, cache.v_pool, cache.tables_device(),
+                        torch.from_numpy(w.lens).cuda(), cfg.q_len, cfg.scale, o, ws)
+        torch.cuda.synchronize()
+        counters = ws[:cfg.batch * cfg.num_kv_heads * 4]
+        assert int(counters.count_nonzero()) == 0
+        if first is None:
+            first = out_bits(o)
+            assert_close(out_to_f64(o, "bf16"), ref, "bf16", f"repeat {key}")
+        else:
+            assert np.array_equal(out_bits(o), first)
+
+
 @pytest.mark.parametrize("key", ["8b", "verify", "tiny_f32"])
 def test_pool_bytes_and_tables_match_model(key):
     """pa_write_kv (allocation, copy-on-write, scatter) gives the model's pool bit for bit."""
