@@ -193,7 +193,11 @@ typedef struct pa_attn_desc {
                                  PARTITIONS of this many tokens, a multiple of 64 */
   int32_t waves_per_group;    /* wavefronts per workgroup of the main kernel: 0 = chosen
                                  by the library, else 1, 2 or 4 */
-  int32_t reserved[4];        /* must be 0 */
+  int32_t kv_shared;          /* cache hint, results do not depend on it: 0 = every
+                                 physical block is read by one sequence only, so K/V
+                                 loads stream past the caches; 1 = some blocks are
+                                 shared (a common prompt), so K/V loads stay cacheable */
+  int32_t reserved[3];        /* must be 0 */
 } pa_attn_desc;
 
 /* What pa_attention launches for a descriptor (for tests and profiling). */

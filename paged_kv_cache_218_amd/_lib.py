@@ -23,7 +23,8 @@ class AttnDesc(C.Structure):
     _fields_ = [("num_seqs", i32), ("num_q_heads", i32), ("num_kv_heads", i32),
                 ("head_dim", i32), ("block_size", i32), ("max_blocks_per_seq", i32),
                 ("num_blocks", i32), ("dtype", i32), ("max_context", i32), ("path", i32),
-                ("partition_tokens", i32), ("waves_per_group", i32), ("reserved", i32 * 4)]
+                ("partition_tokens", i32), ("waves_per_group", i32), ("kv_shared", i32),
+                ("reserved", i32 * 3)]
 
 
 class AttnPlan(C.Structure):

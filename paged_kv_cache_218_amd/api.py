@@ -153,12 +153,14 @@ def pa_copy_blocks(pool: Pool, k_pool, v_pool, src_dst: np.ndarray, stream=None)
 # -- attention ----------------------------------------------------------------
 
 def make_desc(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
-              dtype, max_context, path=_lib.PA_PATH_AUTO, partition_tokens=0, waves_per_group=0) -> AttnDesc:
+              dtype, max_context, path=_lib.PA_PATH_AUTO, partition_tokens=0, waves_per_group=0,
+              kv_shared=0) -> AttnDesc:
     d = AttnDesc()
     d.num_seqs, d.num_q_heads, d.num_kv_heads = num_seqs, num_q_heads, num_kv_heads
     d.head_dim, d.block_size, d.max_blocks_per_seq = head_dim, block_size, max_blocks_per_seq
     d.num_blocks, d.dtype, d.max_context = num_blocks, dtype, max_context
     d.path, d.partition_tokens, d.waves_per_group = path, partition_tokens, waves_per_group
+    d.kv_shared = kv_shared
     return d
 
 

@@ -42,6 +42,7 @@ class PagedKVCache:
                                  dtype=torch_dtype, device=device)
         self.tables = np.full((num_seqs, max_blocks), -1, dtype=np.int32)
         self.live = [0] * num_seqs
+        self.shared = False   # some block is (or was) in more than one table
 
     # -- writes -----------------------------------------------------------
     def write(self, b: int, start_pos: int, k_new, v_new, stream=None) -> None:
@@ -56,6 +57,7 @@ class PagedKVCache:
             api.pa_block_fork(self.pool, int(self.tables[src, j]))
             self.tables[dst, j] = self.tables[src, j]
         self.live[dst] = n_blocks
+        self.shared = self.shared or n_blocks > 0
 
     def free_seq(self, b: int) -> None:
         for j in range(self.live[b]):
@@ -72,7 +74,7 @@ class PagedKVCache:
              waves_per_group=0):
         return api.make_desc(self.tables.shape[0], num_q_heads, self.hkv, self.d, self.bs,
                              self.tables.shape[1], self.nb, self.dtype, max_context, path, partition_tokens,
-                             waves_per_group)
+                             waves_per_group, int(self.shared))
 
     def attention(self, q, tables_dev, lens_dev, q_len: int, scale: float, max_context: int,
                   path=_lib.PA_PATH_AUTO, partition_tokens=0, waves_per_group=0, out=None, workspace=None,

@@ -36,7 +36,6 @@
 
 #include <algorithm>
 #include <cmath>
-#include <cstdlib>
 
 #include "pa_internal.h"
 
@@ -190,6 +189,16 @@ __device__ void poison_rows(const AttnArgs& a, const Tile& t, int R) {
 //   tokens of one head-dim row of the V^T slice: 16 contiguous bytes.
 constexpr int kStep = 32;  // tokens per MFMA step
 
+// 16-byte K/V load. STREAM: each block is read once per call (no sharing), so
+// the load carries the non-temporal hint and the bytes do not displace the
+// tables, queries and partials in the caches; otherwise (blocks shared by
+// several sequences, e.g. a common prompt) the load is cached normally.
+template <bool STREAM>
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
+}
+
 template <int D>
 struct StepBuf {
   u32x4 k[2][D / 32];  // two 16-token K tiles, D/32 k-steps each
@@ -222,7 +231,7 @@ __device__ __forceinline__ void wave_state_init(WaveState<D, NT>& st) {
 // One wavefront's share of a piece: steps first, first+W, ... < end of
 // sequence b (context L), KV head g. Every step covers 32 tokens; tokens at
 // or past L, and tokens after a row's causal limit, are masked.
-template <int D, int BS, int NT, bool PIPE>
+template <int D, int BS, int NT, bool STREAM>
 __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int first, int end, int W,
                                 WaveState<D, NT>& st) {
   constexpr int KS = D / 32;  // k-steps over the head dim for QK
@@ -278,7 +287,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4 v = {0, 0, 0, 0};
-        if (ok) v = *reinterpret_cast<const u32x4*>(row + 32 * ks);
+        if (ok) v = load16<STREAM>(row + 32 * ks);
         buf.k[i][ks] = v;
       }
     }
@@ -290,7 +299,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         u32x4 v = {0, 0, 0, 0};
-        if (ok) v = *reinterpret_cast<const u32x4*>(base + 16 * dt * BS);
+        if (ok) v = load16<STREAM>(base + 16 * dt * BS);
         buf.v[dt] = v;
       }
     }
@@ -367,28 +376,13 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     }
   };
 
-  if constexpr (PIPE) {
-    // Ping-pong over two register buffers: the loads of the wave's next step
-    // are in flight while the current step is computed.
-    StepBuf<D> bufA, bufB;
-    int s = first;
-    load_step(bufA, s);
-    while (s < end) {
-      if (s + W < end) load_step(bufB, s + W);
-      compute_step(bufA);
-      s += W;
-      if (s >= end) break;
-      if (s + W < end) load_step(bufA, s + W);
-      compute_step(bufB);
-      s += W;
-    }
-  } else {
-    // one buffer: other waves on the SIMD hide this wave's load latency
-    StepBuf<D> buf;
-    for (int s = first; s < end; s += W) {
-      load_step(buf, s);
-      compute_step(buf);
-    }
+  // One step buffer per wave: the other waves on the SIMD (three per SIMD
+  // fit) hide this wave's load latency. (A two-buffer ping-pong was measured
+  // no faster: the extra registers cost a wave per SIMD.)
+  StepBuf<D> buf;
+  for (int s = first; s < end; s += W) {
+    load_step(buf, s);
+    compute_step(buf);
   }
 }
 
@@ -446,7 +440,7 @@ __device__ __forceinline__ void combine_waves(const float* smem, int W, int R, i
 
 // Fixed partitions: workgroup = (sequence, KV head, partition); partitions
 // that do not cover the whole sequence leave partials for lse_merge.
-template <int D, int BS, int NT, bool PIPE>
+template <int D, int BS, int NT, bool STREAM>
 __global__ __launch_bounds__(256, 2) void mfma_attn(AttnArgs a) {
   extern __shared__ float smem[];
   const int W = blockDim.x / 64, wave = threadIdx.x / 64;
@@ -457,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn(AttnArgs a) {
   WaveState<D, NT> st;
   wave_state_init(st);
   const int s0 = t.t0 / kStep, s1 = (t.t1 + kStep - 1) / kStep;
-  mfma_wave_steps<D, BS, NT, PIPE>(a, t.b, t.g, t.L, s0 + wave, s1, W, st);
+  mfma_wave_steps<D, BS, NT, STREAM>(a, t.b, t.g, t.L, s0 + wave, s1, W, st);
   const bool bad = park_states(st, R, smem);
   merge_and_store<uint16_t, D>(a, t, R, R, W, smem, smem + W * R, smem + 2 * W * R, bad);
 }
@@ -480,7 +474,7 @@ __device__ __forceinline__ int64_t owner(int64_t x, int64_t S, int64_t N) {
   return k;
 }
 
-template <int D, int BS, int NT, bool PIPE>
+template <int D, int BS, int NT, bool STREAM>
 __global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
   extern __shared__ float smem[];  // [B+1] step prefix sums, then the parked states
   const int W = blockDim.x / 64, wave = threadIdx.x / 64;
@@ -555,7 +549,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
     const int L = a.lens[b];
     WaveState<D, NT> st;
     wave_state_init(st);
-    mfma_wave_steps<D, BS, NT, PIPE>(a, b, g, L, first + wave, last, W, st);
+    mfma_wave_steps<D, BS, NT, STREAM>(a, b, g, L, first + wave, last, W, st);
     const bool bad = park_states(st, R, park);
     const int64_t seg = int64_t(b) * a.hkv + g;
     const bool whole = first == 0 && last == nb;
@@ -891,7 +885,7 @@ __global__ __launch_bounds__(256) void lse_merge(AttnArgs a) {
 // ---------------------------------------------------------------------------
 struct Plan {
   int path, sched, part_tokens, parts, waves, grid, merge_grid, nt, rows;
-  bool pipe;
+  bool stream;  // K/V loads with the non-temporal hint
   int64_t segments, pieces;  // balanced schedule: segments, partial slots
   size_t ws;
 };
@@ -903,8 +897,9 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   if (!d || !pl) return PA_ERR_INVALID_ARG;
-  for (int k = 0; k < 4; ++k)
+  for (int k = 0; k < 3; ++k)
     if (d->reserved[k] != 0) return PA_ERR_INVALID_ARG;
+  if (d->kv_shared != 0 && d->kv_shared != 1) return PA_ERR_INVALID_ARG;
   if (d->waves_per_group != 0 && d->waves_per_group != 1 && d->waves_per_group != 2 &&
       d->waves_per_group != 4)
     return PA_ERR_INVALID_ARG;
@@ -940,8 +935,7 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   pl->waves = waves;
   pl->nt = rows > 16 ? 2 : 1;
   pl->rows = int(rows);
-  pl->pipe = pl->nt == 1;
-  if (const char* e = getenv("PA_EXP_PIPE")) pl->pipe = e[0] == '1';
+  pl->stream = d->kv_shared == 0;
   const bool balanced = path == PA_PATH_MFMA && d->partition_tokens == 0 &&
                         d->num_seqs <= kMaxBalancedSeqs;
   if (balanced) {
@@ -1022,17 +1016,17 @@ pa_status launch_main(const Plan& pl, int dtype, int num_seqs, const AttnArgs& a
   const size_t lds = lds_bytes(pl, D, num_seqs);
   if (pl.path == PA_PATH_MFMA && pl.sched == PA_SCHED_BALANCED) {
     if (pl.nt == 1)
-      return pl.pipe ? launch(mfma_attn_balanced<D, BS, 1, true>, pl, lds, args, s)
-                     : launch(mfma_attn_balanced<D, BS, 1, false>, pl, lds, args, s);
-    return pl.pipe ? launch(mfma_attn_balanced<D, BS, 2, true>, pl, lds, args, s)
-                   : launch(mfma_attn_balanced<D, BS, 2, false>, pl, lds, args, s);
+      return pl.stream ? launch(mfma_attn_balanced<D, BS, 1, true>, pl, lds, args, s)
+                       : launch(mfma_attn_balanced<D, BS, 1, false>, pl, lds, args, s);
+    return pl.stream ? launch(mfma_attn_balanced<D, BS, 2, true>, pl, lds, args, s)
+                     : launch(mfma_attn_balanced<D, BS, 2, false>, pl, lds, args, s);
   }
   if (pl.path == PA_PATH_MFMA) {
     if (pl.nt == 1)
-      return pl.pipe ? launch(mfma_attn<D, BS, 1, true>, pl, lds, args, s)
-                     : launch(mfma_attn<D, BS, 1, false>, pl, lds, args, s);
-    return pl.pipe ? launch(mfma_attn<D, BS, 2, true>, pl, lds, args, s)
-                   : launch(mfma_attn<D, BS, 2, false>, pl, lds, args, s);
+      return pl.stream ? launch(mfma_attn<D, BS, 1, true>, pl, lds, args, s)
+                       : launch(mfma_attn<D, BS, 1, false>, pl, lds, args, s);
+    return pl.stream ? launch(mfma_attn<D, BS, 2, true>, pl, lds, args, s)
+                     : launch(mfma_attn<D, BS, 2, false>, pl, lds, args, s);
   }
   if (dtype == PA_DTYPE_F32) return launch(valu_attn<float, D, BS>, pl, lds, args, s);
   return launch(valu_attn<uint16_t, D, BS>, pl, lds, args, s);
