@@ -81,6 +81,89 @@ def cpu_baseline(w, budget_s: float = 15.0):
     }
 
 
+def kernel_name(cfg, plan, desc) -> str:
+    """Name of the main kernel pa_attention launches for this plan (as rocprofv3 shows it)."""
+    if plan.path == 1:
+        t = "float" if cfg.dtype == "f32" else "unsigned short"
+        return f"valu_attn<{t}, {cfg.head_dim}, {cfg.block_size}>"
+    base = "mfma_attn_balanced" if plan.schedule == 1 else "mfma_attn"
+    nt = 2 if cfg.group * cfg.q_len > 16 else 1
+    stream = "false" if desc.kv_shared else "true"
+    return f"{base}<{cfg.head_dim}, {cfg.block_size}, {nt}, {stream}>"
+
+
+def source_digest() -> str:
+    """sha256 of the HIP sources: counters taken on other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_218_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of the main kernel from committed rocprofv3 counter
+    runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a
+    copy of known size), if they were taken on the current sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != source_digest() or rec.get("kernel") != kernel:
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
+def _pmc_rows(run_dir):
+    import csv
+    path = os.path.join(run_dir, "run_counter_collection.csv")
+    return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(open(path))]
+
+
+def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_bytes: int = 2**30):
+    """Turn two rocprofv3 --pmc runs of `bench.py --copy-probe` (FETCH_SIZE,
+    then WRITE_SIZE; KiB per dispatch) into HBM bytes per launch of the main
+    kernel. Each counter is scaled by copy_bytes over what it reads for the
+    copy probe's dispatches (a device-to-device copy of copy_bytes)."""
+    import statistics
+    import workloads
+    import paged_kv_cache_218_amd as pa
+    cfg = workloads.CONFIGS[workload]
+    lens = workloads.context_lengths(cfg)
+    nb = workloads.pool_blocks(cfg, lens)
+    max_blocks = int(-(-int(lens.max()) // cfg.block_size))
+    desc = pa.make_desc(cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size,
+                        max_blocks, nb, pa.PA_DTYPE_F32 if cfg.dtype == "f32" else pa.PA_DTYPE_BF16,
+                        int(lens.max()), 0, max(cfg.partition_tokens, 0), 0, int(cfg.prefix_len > 0))
+    plan = pa.pa_attention_plan(desc, cfg.q_len)
+    kernel = kernel_name(cfg, plan, desc)
+    out = {"workload": workload, "kernel": kernel, "source_sha256": source_digest(),
+           "algorithmic_bytes": algorithmic_bytes(cfg, lens)}
+    for name, d in (("fetch", fetch_dir), ("write", write_dir)):
+        rows = _pmc_rows(d)
+        copy = [v for k, v in rows if "copyBuffer" in k and v * 1024 > 0.25 * copy_bytes]
+        main = [v for k, v in rows if kernel in k]
+        if not copy or not main:
+            raise SystemExit(f"{d}: no copy-probe or {kernel} dispatches")
+        factor = copy_bytes / (statistics.median(copy) * 1024)
+        out[f"{name}_kib_per_launch"] = statistics.mean(main)
+        out[f"{name}_dispatches"] = len(main)
+        out[f"{name}_copy_kib"] = statistics.median(copy)
+        out[f"{name}_scale"] = factor
+    tb = (out["fetch_kib_per_launch"] * 1024 * out["fetch_scale"]
+          + out["write_kib_per_launch"] * 1024 * out["write_scale"])
+    out["traffic_bytes_per_launch"] = int(round(tb))
+    out["traffic_over_algorithmic"] = tb / out["algorithmic_bytes"]
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def _sub_cfg(cfg, batch):
     from dataclasses import replace
     return replace(cfg, batch=batch)
@@ -119,7 +202,12 @@ def main():
     ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup (0: library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.workload, *args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(sharding is described in DESIGN.md, not implemented)", file=sys.stderr)
@@ -166,15 +254,16 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = ev0.elapsed_time(ev1) / args.steps
-    # per-launch time of the main kernel alone (only separable when there is no merge pass)
-    main_ms = ms if plan.num_partitions == 1 else None
+    # per-launch time of the main kernel alone (one kernel per step unless a
+    # separate merge kernel runs after it)
+    main_ms = ms if plan.merge_grid == 0 else None
 
     nbytes = algorithmic_bytes(cfg, w.lens)
     gbs = nbytes / (ms * 1e-3) / 1e9
     tokens = cfg.batch * cfg.q_len / (ms * 1e-3)
     path_name = {1: "valu", 2: "mfma"}[plan.path]
-    kernel = (f"mfma_attn<{cfg.head_dim},{cfg.block_size},{2 if cfg.group * cfg.q_len > 16 else 1}>"
-              if plan.path == 2 else f"valu_attn<{cfg.dtype},{cfg.head_dim},{cfg.block_size}>")
+    kernel = kernel_name(cfg, plan, desc)
+    traffic = committed_traffic(cfg.name, kernel)
     roof_ms = main_ms if main_ms is not None else ms
     result = {
         "metric": METRIC,
@@ -195,6 +284,7 @@ def main():
             "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
             "block_size": cfg.block_size, "num_blocks": w.num_blocks, "prefix_len": cfg.prefix_len,
             "path": path_name, "partition_tokens": plan.partition_tokens,
+            "schedule": {0: "partitions", 1: "balanced"}[plan.schedule], "kv_shared": int(desc.kv_shared),
             "partitions": plan.num_partitions, "waves_per_group": plan.waves_per_group,
             "grid": plan.grid, "merge_grid": plan.merge_grid,
         },
@@ -210,7 +300,7 @@ def main():
             "unit": "GB/s",
             "frac": round(nbytes / (roof_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "launch_us": round(roof_ms * 1e3, 2),
-            "traffic": None,
+            "traffic": traffic,
             "note": ("one kernel per step: launch time from HIP events over the timed region"
                      if main_ms is not None else
                      "partition kernel + merge kernel per step: time is the pair's"),

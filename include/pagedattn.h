@@ -207,8 +207,9 @@ typedef struct pa_attn_plan {
   int32_t partition_tokens;   /* PARTITIONS: tokens per partition (0 for BALANCED) */
   int32_t num_partitions;     /* PARTITIONS: partitions per sequence (1 = no merge pass) */
   int32_t waves_per_group;    /* wavefronts per workgroup of the main kernel */
-  int32_t grid;               /* workgroups of the main kernel (BALANCED: the upper
-                                 bound; the launch uses the device's resident capacity) */
+  int32_t grid;               /* workgroups of the main kernel; BALANCED: the resident
+                                 capacity of the current device for that kernel (an
+                                 upper bound when no device is available) */
   int32_t merge_grid;         /* workgroups of the merge kernel (0 if none) */
   size_t workspace_bytes;     /* workspace pa_attention needs */
 } pa_attn_plan;

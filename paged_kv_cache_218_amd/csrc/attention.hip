@@ -1000,36 +1000,51 @@ int resident_groups(const void* kernel, int threads, size_t lds) {
   return per_cu * cus;
 }
 
-template <typename K>
-pa_status launch(K kernel, const Plan& pl, size_t lds, const AttnArgs& args, hipStream_t s) {
-  int grid = pl.grid;
-  if (pl.sched == PA_SCHED_BALANCED) {
-    const int fit = resident_groups(reinterpret_cast<const void*>(kernel), 64 * pl.waves, lds);
-    grid = std::max(1, std::min(grid, fit > 0 ? fit : grid));
-  }
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * pl.waves), lds, s, args);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
-}
-
+// The main kernel a plan launches (one template instance per shape).
 template <int D, int BS>
-pa_status launch_main(const Plan& pl, int dtype, int num_seqs, const AttnArgs& args, hipStream_t s) {
-  const size_t lds = lds_bytes(pl, D, num_seqs);
+const void* main_kernel(const Plan& pl, int dtype) {
   if (pl.path == PA_PATH_MFMA && pl.sched == PA_SCHED_BALANCED) {
     if (pl.nt == 1)
-      return pl.stream ? launch(mfma_attn_balanced<D, BS, 1, true>, pl, lds, args, s)
-                       : launch(mfma_attn_balanced<D, BS, 1, false>, pl, lds, args, s);
-    return pl.stream ? launch(mfma_attn_balanced<D, BS, 2, true>, pl, lds, args, s)
-                     : launch(mfma_attn_balanced<D, BS, 2, false>, pl, lds, args, s);
+      return pl.stream ? reinterpret_cast<const void*>(mfma_attn_balanced<D, BS, 1, true>)
+                       : reinterpret_cast<const void*>(mfma_attn_balanced<D, BS, 1, false>);
+    return pl.stream ? reinterpret_cast<const void*>(mfma_attn_balanced<D, BS, 2, true>)
+                     : reinterpret_cast<const void*>(mfma_attn_balanced<D, BS, 2, false>);
   }
   if (pl.path == PA_PATH_MFMA) {
     if (pl.nt == 1)
-      return pl.stream ? launch(mfma_attn<D, BS, 1, true>, pl, lds, args, s)
-                       : launch(mfma_attn<D, BS, 1, false>, pl, lds, args, s);
-    return pl.stream ? launch(mfma_attn<D, BS, 2, true>, pl, lds, args, s)
-                     : launch(mfma_attn<D, BS, 2, false>, pl, lds, args, s);
+      return pl.stream ? reinterpret_cast<const void*>(mfma_attn<D, BS, 1, true>)
+                       : reinterpret_cast<const void*>(mfma_attn<D, BS, 1, false>);
+    return pl.stream ? reinterpret_cast<const void*>(mfma_attn<D, BS, 2, true>)
+                     : reinterpret_cast<const void*>(mfma_attn<D, BS, 2, false>);
   }
-  if (dtype == PA_DTYPE_F32) return launch(valu_attn<float, D, BS>, pl, lds, args, s);
-  return launch(valu_attn<uint16_t, D, BS>, pl, lds, args, s);
+  return dtype == PA_DTYPE_F32 ? reinterpret_cast<const void*>(valu_attn<float, D, BS>)
+                               : reinterpret_cast<const void*>(valu_attn<uint16_t, D, BS>);
+}
+
+const void* main_kernel_for(const Plan& pl, int dtype, int D, int BS) {
+  if (D == 64) return BS == 16 ? main_kernel<64, 16>(pl, dtype) : main_kernel<64, 32>(pl, dtype);
+  return BS == 16 ? main_kernel<128, 16>(pl, dtype) : main_kernel<128, 32>(pl, dtype);
+}
+
+// Workgroups the main kernel is launched with: for the balanced schedule the
+// device's resident capacity for that kernel (capped by the plan's bound).
+int launch_grid(const Plan& pl, const pa_attn_desc* d) {
+  if (pl.sched != PA_SCHED_BALANCED) return pl.grid;
+  const void* k = main_kernel_for(pl, d->dtype, d->head_dim, d->block_size);
+  const int fit = resident_groups(k, 64 * pl.waves, lds_bytes(pl, d->head_dim, d->num_seqs));
+  return std::max(1, std::min(pl.grid, fit > 0 ? fit : pl.grid));
+}
+
+pa_status launch_main(const Plan& pl, const pa_attn_desc* d, const AttnArgs& args, hipStream_t s) {
+  const void* k = main_kernel_for(pl, d->dtype, d->head_dim, d->block_size);
+  const size_t lds = lds_bytes(pl, d->head_dim, d->num_seqs);
+  const int grid = launch_grid(pl, d);
+  void* kargs[] = {const_cast<AttnArgs*>(&args)};
+  if (hipLaunchKernel(k, dim3(grid), dim3(64 * pl.waves), kargs, lds, s) != hipSuccess) {
+    (void)hipGetLastError();
+    return PA_ERR_HIP;
+  }
+  return PA_OK;
 }
 
 template <int D>
@@ -1054,7 +1069,7 @@ extern "C" pa_status pa_attention_plan(const pa_attn_desc* desc, int32_t q_len, 
   out->partition_tokens = pl.part_tokens;
   out->num_partitions = pl.parts;
   out->waves_per_group = pl.waves;
-  out->grid = pl.grid;
+  out->grid = launch_grid(pl, desc);
   out->merge_grid = pl.merge_grid;
   out->workspace_bytes = pl.ws;
   return PA_OK;
@@ -1111,11 +1126,8 @@ extern "C" pa_status pa_attention(const pa_attn_desc* desc, const void* q, const
   args.part_tokens = pl.part_tokens;
   args.scale_log2 = scale * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int D = desc->head_dim, BS = desc->block_size, B = desc->num_seqs;
-  if (D == 64)
-    st = BS == 16 ? launch_main<64, 16>(pl, desc->dtype, B, args, s) : launch_main<64, 32>(pl, desc->dtype, B, args, s);
-  else
-    st = BS == 16 ? launch_main<128, 16>(pl, desc->dtype, B, args, s) : launch_main<128, 32>(pl, desc->dtype, B, args, s);
+  st = launch_main(pl, desc, args, s);
   if (st != PA_OK || pl.merge_grid == 0) return st;
-  return D == 64 ? launch_merge<64>(pl, desc->dtype, args, s) : launch_merge<128>(pl, desc->dtype, args, s);
+  return desc->head_dim == 64 ? launch_merge<64>(pl, desc->dtype, args, s)
+                              : launch_merge<128>(pl, desc->dtype, args, s);
 }
