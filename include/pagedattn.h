@@ -31,10 +31,15 @@
  *   - "host" pointers are CPU memory, "device" pointers are GPU memory on the
  *     current HIP device; all buffers are owned by the caller unless stated.
  *   - Pool layout (device memory, caller-owned, element type = pool dtype):
- *       k_pool: [num_blocks][num_kv_heads][block_size][head_dim]
+ *       k_pool: [num_blocks][num_kv_heads][head_dim/32][block_size][32]
  *       v_pool: [num_blocks][num_kv_heads][head_dim][block_size]
  *     One (block, kv head) slice of K or V is contiguous (block_size*head_dim
- *     elements); V keeps each head dimension's tokens adjacent.
+ *     elements). Within a K slice the head dimension is cut into 32-element
+ *     slabs, each holding the block's tokens back to back; within a V slice
+ *     each head-dimension element keeps the block's tokens adjacent. Element
+ *     (token t, dim c) of block b, KV head h is at
+ *       K: (((b*H_kv + h)*(head_dim/32) + c/32)*block_size + t)*32 + c%32
+ *       V: ((b*H_kv + h)*head_dim + c)*block_size + t
  *   - bf16 is IEEE bfloat16 stored as uint16; f32 is IEEE binary32.
  */
 #ifndef PAGEDATTN_H

@@ -2,8 +2,10 @@
 
 Layout (the library's documented pool layout, so that device pools can be
 compared with this model byte for byte):
-    k[block][kv_head][slot_in_block][dim]      ([NB][H_kv][bs][d])
-    v[block][kv_head][dim][slot_in_block]      ([NB][H_kv][d][bs])
+    k[block][kv_head][dim // 32][slot_in_block][dim % 32]   ([NB][H_kv][d/32][bs][32])
+    v[block][kv_head][dim][slot_in_block]                   ([NB][H_kv][d][bs])
+(K's head dimension is cut into 32-element slabs; each slab keeps the block's
+tokens one after another.)
 Physical slot s = block * bs + offset holds token position p of a sequence
 whose table maps logical block p // bs to ``block`` and offset = p % bs
 (block table / free pool: Part 8, "Phân Tích Cơ Cấu Bộ Nhớ Của KV Cache"
@@ -25,7 +27,8 @@ class HostPool:
         self.nb, self.bs, self.hkv, self.d, self.dtype = num_blocks, block_size, num_kv_heads, head_dim, dtype
         np_t = np.float32 if dtype == "f32" else np.uint16
         fill = (np.float32(np.nan) if dtype == "f32" else _NAN_BITS["bf16"]) if fill_nan else 0
-        self.k = np.full((num_blocks, num_kv_heads, block_size, head_dim), fill, dtype=np_t)
+        assert head_dim % 32 == 0
+        self.k = np.full((num_blocks, num_kv_heads, head_dim // 32, block_size, 32), fill, dtype=np_t)
         self.v = np.full((num_blocks, num_kv_heads, head_dim, block_size), fill, dtype=np_t)
 
     def copy_block(self, src: int, dst: int) -> None:
@@ -37,8 +40,16 @@ class HostPool:
         slots = np.asarray(slots, dtype=np.int64)
         blk, off = slots // self.bs, slots % self.bs
         # slots are distinct, so the fancy-index assignment has no collisions
-        self.k[blk, :, off, :] = k_new
+        n = slots.size
+        self.k[blk, :, :, off, :] = np.asarray(k_new).reshape(n, self.hkv, self.d // 32, 32)
         self.v[blk, :, :, off] = v_new
+
+    def put_token(self, blk: int, off: int, k_row=None, v_row=None) -> None:
+        """Store one token's K and/or V rows ([H_kv][d]) in slot off of block blk."""
+        if k_row is not None:
+            self.k[blk, :, :, off, :] = np.asarray(k_row).reshape(self.hkv, self.d // 32, 32)
+        if v_row is not None:
+            self.v[blk, :, :, off] = v_row
 
     def write(self, model: BlockPoolModel, table, capacity: int, num_blocks: int,
               start_pos: int, k_new: np.ndarray, v_new: np.ndarray) -> int:
@@ -56,8 +67,8 @@ class HostPool:
         pos = np.arange(ctx_len)
         blk = np.asarray(table, dtype=np.int64)[pos // self.bs]
         off = pos % self.bs
-        k = self.k[blk, :, off, :]                      # [L][H_kv][d]
-        v = self.v[blk, :, :, off]                      # [L][H_kv][d]
+        k = self.k[blk, :, :, off, :].reshape(ctx_len, self.hkv, self.d)   # [L][H_kv][d]
+        v = self.v[blk, :, :, off]                                         # [L][H_kv][d]
         return k, v
 
     def gather_head(self, table, ctx_len: int, g: int):
@@ -65,4 +76,4 @@ class HostPool:
         pos = np.arange(ctx_len)
         blk = np.asarray(table, dtype=np.int64)[pos // self.bs]
         off = pos % self.bs
-        return self.k[blk, g, off, :], self.v[blk, g, :, off]
+        return self.k[blk, g, :, off, :].reshape(ctx_len, self.d), self.v[blk, g, :, off]

@@ -1,7 +1,7 @@
 """A batch of sequences over one paged KV pool, driven through the C ABI.
 
 Holds the pool handle (host refcounts and free list), the device K/V pools
-(torch tensors, pool layout k [NB][H_kv][bs][d], v [NB][H_kv][d][bs]), the
+(torch tensors, pool layout k [NB][H_kv][d/32][bs][32], v [NB][H_kv][d][bs]), the
 host block tables and each sequence's live-block count. Every operation is
 one ``pa_*`` call; torch only provides the device memory and the stream.
 """
@@ -36,7 +36,7 @@ class PagedKVCache:
         self.pool = api.pa_pool_create(num_blocks, block_size, num_kv_heads, head_dim, self.dtype,
                                        initial_free_order)
         fill = float("nan") if fill_nan else 0.0
-        self.k_pool = torch.full((num_blocks, num_kv_heads, block_size, head_dim), fill,
+        self.k_pool = torch.full((num_blocks, num_kv_heads, head_dim // 32, block_size, 32), fill,
                                  dtype=torch_dtype, device=device)
         self.v_pool = torch.full((num_blocks, num_kv_heads, head_dim, block_size), fill,
                                  dtype=torch_dtype, device=device)

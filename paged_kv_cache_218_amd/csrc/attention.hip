@@ -277,17 +277,20 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     buf.ok = blk0 >= 0 && blk0 < a.nb && blk1 >= 0 && blk1 < a.nb;
     const int64_t o0 = buf.ok ? (int64_t(blk0) * a.hkv + g) * head_stride : 0;
     const int64_t o1 = buf.ok ? (int64_t(blk1) * a.hkv + g) * head_stride : 0;
-    // K tiles: A operand, token of row n in tile i
+    // K tiles: A operand, token of row n in tile i. K slab ks holds head-dim
+    // elements 32ks..32ks+31 of the block's tokens back to back (64 B each),
+    // so one load instruction reads tokens {0-3, 8-11, 16-19, 24-27} (tile 0)
+    // or {4-7, ...} (tile 1) of slab ks: four runs of 256 contiguous bytes.
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int tok = 8 * (n >> 2) + 4 * i + (n & 3);
       const bool second = BS == 16 && tok >= 16;
-      const uint16_t* row = kp + (second ? o1 : o0) + (tok & (BS - 1)) * D + 8 * j;
+      const uint16_t* row = kp + (second ? o1 : o0) + (tok & (BS - 1)) * 32 + 8 * j;
       const bool ok = buf.ok && (!second || have1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4 v = {0, 0, 0, 0};
-        if (ok) v = load16<STREAM>(row + 32 * ks);
+        if (ok) v = load16<STREAM>(row + ks * (BS * 32));
         buf.k[i][ks] = v;
       }
     }
@@ -696,9 +699,10 @@ __global__ __launch_bounds__(256) void valu_attn(AttnArgs a) {
     const bool blk_ok = blk >= 0 && blk < a.nb;
     if (in && !blk_ok) poisoned = true;
     if (in && blk_ok) {
-      const T* krow = kp + (int64_t(blk) * a.hkv + t.g) * head_stride + (tok % BS) * D;
+      // K slice: 32-element head-dim slabs, each [bs][32]
+      const T* krow = kp + (int64_t(blk) * a.hkv + t.g) * head_stride + (tok % BS) * 32;
       for (int c0 = 0; c0 < D; c0 += VEC) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(krow + c0);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(krow + (c0 / 32) * (BS * 32) + c0 % 32);
         float kv[VEC];
         if constexpr (sizeof(T) == 4) {
 #pragma unroll

@@ -6,7 +6,7 @@
 // first gives the writer its own copy; the host plan (pool.cpp) takes those
 // decisions, these kernels move the bytes.
 //
-// Pool layout: k_pool [NB][H_kv][bs][d], v_pool [NB][H_kv][d][bs].
+// Pool layout: k_pool [NB][H_kv][d/32][bs][32], v_pool [NB][H_kv][d][bs].
 // Both kernels take their block ids by value (kernel arguments), so a write
 // needs no device-side staging buffer.
 #include <hip/hip_runtime.h>
@@ -51,9 +51,11 @@ __global__ void scatter_kernel(T* __restrict__ k_pool, T* __restrict__ v_pool,
   const int64_t blk = ids.id[pos / bs - first_logical];
   const int off = pos % bs;
   const int64_t src = (int64_t(tok0 + i) * hkv + h) * d + int64_t(c) * VEC;
-  // K row: contiguous 16 bytes
-  *reinterpret_cast<u32x4*>(k_pool + ((blk * hkv + h) * bs + off) * d + int64_t(c) * VEC) =
-      *reinterpret_cast<const u32x4*>(k_new + src);
+  // K: elements c*VEC .. c*VEC+VEC-1 of the row sit in slab (c*VEC)/32 at the
+  // token's 32-element run (16 contiguous bytes, never straddling a slab)
+  const int e0 = c * VEC;
+  *reinterpret_cast<u32x4*>(k_pool + ((blk * hkv + h) * (d / 32) + e0 / 32) * (int64_t(bs) * 32) +
+                            off * 32 + e0 % 32) = *reinterpret_cast<const u32x4*>(k_new + src);
   // V: element e of the chunk goes to row (c*VEC + e) of the [d][bs] slice
   T* vdst = v_pool + ((blk * hkv + h) * d + int64_t(c) * VEC) * bs + off;
 #pragma unroll

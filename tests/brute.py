@@ -17,7 +17,7 @@ def scalar(x, dtype):
 
 
 def brute_attention(q, k_pool, v_pool, tables, lens, q_len, scale, block_size, dtype):
-    """q: [B][q_len][H_q][d]; k_pool [NB][H_kv][bs][d]; v_pool [NB][H_kv][d][bs].
+    """q: [B][q_len][H_q][d]; k_pool [NB][H_kv][d/32][bs][32]; v_pool [NB][H_kv][d][bs].
     Returns nested lists [B][q_len][H_q][d] of floats."""
     B, _, Hq, d = q.shape
     Hkv = k_pool.shape[1]
@@ -35,7 +35,7 @@ def brute_attention(q, k_pool, v_pool, tables, lens, q_len, scale, block_size, d
                 for t in range(L - q_len + i + 1):
                     blk = int(tables[b][t // block_size])
                     off = t % block_size
-                    kr = [scalar(k_pool[blk, g, off, c], dtype) for c in range(d)]
+                    kr = [scalar(k_pool[blk, g, c // 32, off, c % 32], dtype) for c in range(d)]
                     vrows.append([scalar(v_pool[blk, g, c, off], dtype) for c in range(d)])
                     scores.append(scale * math.fsum(qv[c] * kr[c] for c in range(d)))
                 mx = max(scores)

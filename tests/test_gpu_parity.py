@@ -49,6 +49,49 @@ def test_parity_small(key, path, part):
     assert_close(out_to_f64(out, w.cfg.dtype), ref, w.cfg.dtype, key)
 
 
+SHAPES = [
+    # dtype, q_len, H_q, H_kv, d, bs, context lengths
+    ("bf16", 1, 8, 8, 64, 16, (5, 70, 300)),         # one query head per KV head, d 64
+    ("bf16", 1, 16, 1, 64, 32, (31, 32, 33, 200)),   # 16 query heads on one KV head
+    ("bf16", 4, 16, 2, 128, 32, (40, 129)),          # 8 x 4 = 32 rows: both row tiles full
+    ("bf16", 2, 8, 2, 128, 16, (2, 17, 600)),        # context equal to q_len
+    ("bf16", 8, 4, 1, 64, 16, (8, 9, 100)),          # 8 drafted tokens
+    ("f32", 3, 4, 2, 128, 32, (3, 50, 301)),         # fp32 verification
+    ("f32", 1, 16, 1, 128, 16, (1, 999)),            # fp32, 16 rows
+    ("bf16", 1, 4, 2, 64, 32, (1, 64, 65)),          # bf16 d 64, block 32
+]
+
+
+def shape_cases():
+    out = []
+    for i, (dt, ql, hq, hkv, d, bs, lens) in enumerate(SHAPES):
+        rows = hq // hkv * ql
+        paths = ([MFMA] if dt == "bf16" and rows <= 32 else []) + ([VALU] if rows <= 16 else [])
+        for path in paths:
+            for pt in (0, 64):
+                out.append((i, path, pt))
+    return out
+
+
+_shape_cache = {}
+
+
+@pytest.mark.parametrize("i,path,pt", shape_cases(),
+                         ids=[f"s{i}-{'mfma' if p == 2 else 'valu'}-pt{t}" for i, p, t in shape_cases()])
+def test_parity_shapes(i, path, pt):
+    if i not in _shape_cache:
+        dt, ql, hq, hkv, d, bs, lens = SHAPES[i]
+        cfg = workloads.Config(f"shape{i}", 100 + i, batch=len(lens), q_len=ql, num_q_heads=hq,
+                               num_kv_heads=hkv, head_dim=d, block_size=bs, dtype=dt, lens=lens,
+                               pool_slack=1.5)
+        w = workloads.generate(cfg)
+        _shape_cache[i] = (w, oracle_out(w))
+    w, ref = _shape_cache[i]
+    print(f"shape {SHAPES[i]} path {path} part {pt}", flush=True)
+    out, _ = run_gpu(w, path=path, partition_tokens=pt)
+    assert_close(out_to_f64(out, w.cfg.dtype), ref, w.cfg.dtype, f"shape {i}")
+
+
 WAVE_CASES = [(k, wv) for k in ("8b", "70b", "verify", "long") for wv in (1, 2)]
 
 

@@ -70,21 +70,19 @@ def test_printed_block_tables(case):
     bs, n, table = case["block_size"], case["tokens"], case["table"]
     nb = max(table) + 1
     rng = np.random.default_rng(1)
-    k = rng.standard_normal((n, 2, 8)).astype(np.float32)
-    v = rng.standard_normal((n, 2, 8)).astype(np.float32)
-    pool = HostPool(nb, bs, 2, 8, "f32")
+    k = rng.standard_normal((n, 2, 32)).astype(np.float32)
+    v = rng.standard_normal((n, 2, 32)).astype(np.float32)
+    pool = HostPool(nb, bs, 2, 32, "f32")
     # place token p in physical block table[p // bs], slot p % bs, as the diagram draws it
     for p in range(n):
-        blk, off = table[p // bs], p % bs
-        pool.k[blk, :, off, :] = k[p]
-        pool.v[blk, :, :, off] = v[p]
+        pool.put_token(table[p // bs], p % bs, k[p], v[p])
     kg, vg = pool.gather(table, n)
     assert np.array_equal(kg, k) and np.array_equal(vg, v)
     # every other physical block is untouched (still NaN)
     others = [b for b in range(nb) if b not in table]
     assert np.isnan(pool.k[others]).all() and np.isnan(pool.v[others]).all()
     # the oracle sees the logical sequence: equal to attention on the unpaged arrays
-    q = rng.standard_normal((1, 1, 4, 8)).astype(np.float32)
+    q = rng.standard_normal((1, 1, 4, 32)).astype(np.float32)
     out = oatt.attention_paged(q, pool, [table], [n], 1, 0.3)
     ref = oatt.attention_contiguous(q[0], k, v, 1, 4, 2, 0.3, "f32")
     assert np.array_equal(out[0], ref)
@@ -93,10 +91,10 @@ def test_printed_block_tables(case):
 # -- brute force on tiny inputs ---------------------------------------------
 
 @pytest.mark.parametrize("dtype,q_len,hq,hkv,d,bs,lens", [
-    ("f32", 1, 4, 2, 8, 4, (1, 5, 9)),
-    ("bf16", 1, 8, 2, 4, 4, (3, 8, 13)),
-    ("f32", 3, 6, 3, 5, 2, (3, 7)),
-    ("bf16", 4, 4, 1, 6, 8, (4, 11, 20)),
+    ("f32", 1, 4, 2, 32, 4, (1, 5, 9)),
+    ("bf16", 1, 8, 2, 32, 4, (3, 8, 13)),
+    ("f32", 3, 6, 3, 32, 2, (3, 7)),
+    ("bf16", 4, 4, 1, 64, 8, (4, 11, 20)),
 ])
 def test_oracle_vs_brute_force(dtype, q_len, hq, hkv, d, bs, lens):
     cfg = workloads.Config("brute", 90, batch=len(lens), q_len=q_len, num_q_heads=hq,
@@ -202,8 +200,9 @@ def test_causal_rows():
     i = 1
     for t in range(L - cfg.q_len + i + 1, L):
         blk, off = tables[b][t // cfg.block_size], t % cfg.block_size
-        pert.k[blk, :, off, :] = workloads.bf16_bits_from_f32(np.full(cfg.head_dim, 50.0, np.float32))
-        pert.v[blk, :, :, off] = workloads.bf16_bits_from_f32(np.full(cfg.head_dim, -7.0, np.float32))
+        pert.put_token(blk, off,
+                       workloads.bf16_bits_from_f32(np.full((cfg.num_kv_heads, cfg.head_dim), 50.0, np.float32)),
+                       workloads.bf16_bits_from_f32(np.full((cfg.num_kv_heads, cfg.head_dim), -7.0, np.float32)))
     out2 = oatt.attention_paged_seq(w.seqs[b].q, pert, tables[b], L, cfg.q_len, cfg.num_q_heads, cfg.scale)
     assert np.array_equal(out2[:i + 1], out[b, :i + 1])
     assert not np.allclose(out2[i + 1:], out[b, i + 1:])

@@ -19,8 +19,8 @@ from tests import test_allocator_model as apins
 def run_pins():
     """Run a representative set of pins; return the names of those that fail."""
     checks = {
-        "brute": lambda: pins.test_oracle_vs_brute_force("bf16", 4, 4, 1, 6, 8, (4, 11, 20)),
-        "brute_gqa": lambda: pins.test_oracle_vs_brute_force("bf16", 1, 8, 2, 4, 4, (3, 8, 13)),
+        "brute": lambda: pins.test_oracle_vs_brute_force("bf16", 4, 4, 1, 64, 8, (4, 11, 20)),
+        "brute_gqa": lambda: pins.test_oracle_vs_brute_force("bf16", 1, 8, 2, 32, 4, (3, 8, 13)),
         "sdpa_verify": lambda: pins.test_oracle_vs_torch_sdpa("prefix_verify"),
         "sdpa_decode": lambda: pins.test_oracle_vs_torch_sdpa("llama3_8b_decode"),
         "tables": lambda: [pins.test_printed_block_tables(c) for c in
@@ -71,12 +71,13 @@ def _gather_mutant(kind):
         pos = np.arange(ctx_len)
         blk = np.asarray(table, dtype=np.int64)[pos // self.bs]
         off = pos % self.bs
+        kr = lambda o: self.k[blk, g, :, o, :].reshape(ctx_len, self.d)
         if kind == "v_transposed":
             flat = self.v[:, g].transpose(0, 2, 1)          # pretend v were [bs][d] row-major
-            return self.k[blk, g, off, :], flat.reshape(self.nb, self.d, self.bs)[blk, :, off]
+            return kr(off), flat.reshape(self.nb, self.d, self.bs)[blk, :, off]
         if kind == "offset":
             off = (pos // self.bs) % self.bs
-        return self.k[blk, g, off, :], self.v[blk, g, :, off]
+        return kr(off), self.v[blk, g, :, off]
     return gather_head
 
 
