@@ -642,8 +642,18 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
 // per row, probabilities go through LDS, and lane l then accumulates head-dim
 // elements l and l + 64 of every row over the step's tokens from the V^T
 // slices (16-byte loads of adjacent tokens).
+// bf16: both contractions use v_dot2_f32_bf16 on packed pairs: q.k on the raw
+// bf16 pairs of q (LDS) and of the K row (no unpacking), P.V on pairs of
+// adjacent tokens, with the probabilities rounded to bf16 (the row sum uses
+// the rounded values). f32: plain FMAs.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                         false);
+}
+
 template <typename T, int D, int BS>
 __global__ __launch_bounds__(256) void valu_attn(AttnArgs a) {
+  constexpr bool BF = sizeof(T) == 2;
   constexpr int VEC = 16 / sizeof(T);     // elements per 16-byte load
   constexpr int DPL = D / 64;             // head-dim elements per lane in P.V
   constexpr int RM = kValuMaxRows;
@@ -660,17 +670,32 @@ __global__ __launch_bounds__(256) void valu_attn(AttnArgs a) {
   const T* __restrict__ vp = static_cast<const T*>(a.v_pool);
   const int32_t* __restrict__ table = a.tables + int64_t(t.b) * a.mb;
 
-  // LDS: q_s[RM][D] | p_s[W][RM][64] ; the merge reuses the space after q_s
+  // LDS: q_s (f32: [RM][D] pre-scaled; bf16: [RM][D/2] raw pairs) | p_s per
+  // wave (f32: [RM][64] floats; bf16: [RM][64] bf16); the merge reuses it all
   float* q_s = smem;
   float* p_s = q_s + RM * D;
-  for (int e = threadIdx.x; e < RM * D; e += blockDim.x) {
-    const int r = e / D, c = e % D;
-    float v = 0.f;
-    if (r < R) {
-      const int i = r / a.group, h = t.g * a.group + r % a.group;
-      v = load_f<T>(q + (int64_t(t.b * a.q_len + i) * a.hq + h) * D + c) * a.scale_log2;
+  const uint32_t* q2 = reinterpret_cast<const uint32_t*>(q_s);
+  if constexpr (BF) {
+    uint32_t* qw = reinterpret_cast<uint32_t*>(q_s);
+    for (int e = threadIdx.x; e < RM * D / 2; e += blockDim.x) {
+      const int r = e / (D / 2), c2 = e % (D / 2);
+      uint32_t v = 0;
+      if (r < R) {
+        const int i = r / a.group, h = t.g * a.group + r % a.group;
+        v = reinterpret_cast<const uint32_t*>(q + (int64_t(t.b * a.q_len + i) * a.hq + h) * D)[c2];
+      }
+      qw[e] = v;
     }
-    q_s[e] = v;
+  } else {
+    for (int e = threadIdx.x; e < RM * D; e += blockDim.x) {
+      const int r = e / D, c = e % D;
+      float v = 0.f;
+      if (r < R) {
+        const int i = r / a.group, h = t.g * a.group + r % a.group;
+        v = load_f<T>(q + (int64_t(t.b * a.q_len + i) * a.hq + h) * D + c) * a.scale_log2;
+      }
+      q_s[e] = v;
+    }
   }
   __syncthreads();
 
@@ -683,7 +708,9 @@ __global__ __launch_bounds__(256) void valu_attn(AttnArgs a) {
     for (int k = 0; k < DPL; ++k) acc[r][k] = 0.f;
   }
   bool poisoned = false;
-  float* pw = p_s + wave * RM * 64;
+  float* pw = p_s + wave * RM * 64;                              // f32 probabilities
+  uint16_t* pwh = reinterpret_cast<uint16_t*>(pw);               // bf16 probabilities
+  const uint32_t* pw2 = reinterpret_cast<const uint32_t*>(pw);   // ... as token pairs
   const int64_t head_stride = int64_t(BS) * D;
   const int nsteps = (t.t1 - t.t0 + 63) / 64;
 
@@ -703,24 +730,28 @@ __global__ __launch_bounds__(256) void valu_attn(AttnArgs a) {
       const T* krow = kp + (int64_t(blk) * a.hkv + t.g) * head_stride + (tok % BS) * 32;
       for (int c0 = 0; c0 < D; c0 += VEC) {
         const u32x4 raw = *reinterpret_cast<const u32x4*>(krow + (c0 / 32) * (BS * 32) + c0 % 32);
-        float kv[VEC];
-        if constexpr (sizeof(T) == 4) {
+        if constexpr (BF) {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) kv[e] = __uint_as_float(raw[e]);
+          for (int r = 0; r < RM; ++r) {
+            if (r < R) {
+              const u32x4 qq = *reinterpret_cast<const u32x4*>(q2 + r * (D / 2) + c0 / 2);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sc[r] = dot2_bf16(qq[e], raw[e], sc[r]);
+            }
+          }
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kv[2 * e] = __uint_as_float(raw[e] << 16);
-            kv[2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+          for (int r = 0; r < RM; ++r) {
+            if (r < R) {
+#pragma unroll
+              for (int e = 0; e < VEC; ++e) sc[r] = fmaf(q_s[r * D + c0 + e], __uint_as_float(raw[e]), sc[r]);
+            }
           }
         }
+      }
+      if constexpr (BF) {
 #pragma unroll
-        for (int r = 0; r < RM; ++r) {
-          if (r < R) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) sc[r] = fmaf(q_s[r * D + c0 + e], kv[e], sc[r]);
-          }
-        }
+        for (int r = 0; r < RM; ++r) sc[r] *= a.scale_log2;
       }
     }
     // online softmax per row over the step
@@ -735,12 +766,18 @@ __global__ __launch_bounds__(256) void valu_attn(AttnArgs a) {
       const float m_new = fmaxf(m_run[r], mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = fast_exp2(m_run[r] - m_use);
-      const float pr = fast_exp2(v - m_use);
+      float pr = fast_exp2(v - m_use);
+      if constexpr (BF) {
+        const uint16_t pb = f_to_bf16(pr);
+        pwh[r * 64 + lane] = pb;
+        pr = bf16_to_f(pb);   // the row sum uses the rounded weight
+      } else {
+        pw[r * 64 + lane] = pr;
+      }
       m_run[r] = m_new;
       l_run[r] = l_run[r] * alpha + pr;   // lane-partial sum, reduced at the end
 #pragma unroll
       for (int k = 0; k < DPL; ++k) acc[r][k] *= alpha;
-      pw[r * 64 + lane] = pr;
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -756,25 +793,33 @@ __global__ __launch_bounds__(256) void valu_attn(AttnArgs a) {
       for (int k = 0; k < DPL; ++k) {
         const T* vrow = vslice + int64_t(lane + 64 * k) * BS;
         for (int u0 = 0; u0 < cnt; u0 += VEC) {
-          const u32x4 raw = *reinterpret_cast<const u32x4*>(vrow + u0);
-          float vv[VEC];
-          if constexpr (sizeof(T) == 4) {
+          u32x4 raw = *reinterpret_cast<const u32x4*>(vrow + u0);
+          if constexpr (BF) {
+            // tokens past the context keep their pool bytes (NaN in tests): zero them
+            const int valid = cnt - u0;
+            if (valid < 8) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) vv[e] = __uint_as_float(raw[e]);
+              for (int w4 = 0; w4 < 4; ++w4)
+                raw[w4] &= (2 * w4 + 1 < valid) ? 0xffffffffu : (2 * w4 < valid ? 0x0000ffffu : 0u);
+            }
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+              if (r < R) {
+                const u32x4 pp = *reinterpret_cast<const u32x4*>(pw2 + r * 32 + (kb * BS + u0) / 2);
+#pragma unroll
+                for (int w4 = 0; w4 < 4; ++w4) acc[r][k] = dot2_bf16(pp[w4], raw[w4], acc[r][k]);
+              }
+            }
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              vv[2 * e] = __uint_as_float(raw[e] << 16);
-              vv[2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
-            }
-          }
+            for (int e = 0; e < VEC; ++e) {
+              if (u0 + e < cnt) {
+                const int tt = kb * BS + u0 + e;
+                const float vv = __uint_as_float(raw[e]);
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            if (u0 + e < cnt) {
-              const int tt = kb * BS + u0 + e;
-#pragma unroll
-              for (int r = 0; r < RM; ++r)
-                if (r < R) acc[r][k] = fmaf(pw[r * 64 + tt], vv[e], acc[r][k]);
+                for (int r = 0; r < RM; ++r)
+                  if (r < R) acc[r][k] = fmaf(pw[r * 64 + tt], vv, acc[r][k]);
+              }
             }
           }
         }
@@ -960,8 +1005,11 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   }
   int pt = d->partition_tokens;
   if (pt == 0) {
-    // enough waves to give every compute unit 8 of them, partitions >= 256 tokens
-    const int64_t want = (int64_t(kCUs) * 8 + pairs * waves - 1) / (pairs * waves);
+    // enough waves for two full rounds of the kernel's occupancy (the VALU
+    // kernel runs 16 waves per compute unit; the MFMA one 12), partitions of
+    // at least 256 tokens
+    const int64_t target = int64_t(kCUs) * (path == PA_PATH_VALU ? 32 : 24);
+    const int64_t want = (target + pairs * waves - 1) / (pairs * waves);
     const int max_parts = std::max(1, ceil_div(d->max_context, 256));
     const int parts = int(std::min<int64_t>(std::max<int64_t>(want, 1), max_parts));
     pt = ceil_div(ceil_div(d->max_context, parts), 64) * 64;
