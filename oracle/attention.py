@@ -63,15 +63,20 @@ def attention_contiguous(q, k, v, q_len: int, num_q_heads: int, num_kv_heads: in
     return out
 
 
+def _q_dtype(pool: HostPool, q_dtype):
+    return q_dtype or ("bf16" if pool.dtype == "fp8" else pool.dtype)
+
+
 def attention_paged_seq(q, pool: HostPool, table, ctx_len: int, q_len: int,
-                        num_q_heads: int, scale: float) -> np.ndarray:
-    """One sequence read through its block table: gather, then the definition."""
+                        num_q_heads: int, scale: float, q_dtype: str = None) -> np.ndarray:
+    """One sequence read through its block table: gather, then the definition.
+    An fp8 pool is read as its dequantised values (code value times the
+    token's scale)."""
     G = num_q_heads // pool.hkv
-    qf = to_f64(q, pool.dtype)
+    qf = to_f64(q, _q_dtype(pool, q_dtype))
     out = np.empty(qf.shape, dtype=np.float64)
     for g in range(pool.hkv):
-        kr, vr = pool.gather_head(table, ctx_len, g)
-        kf, vf = to_f64(kr, pool.dtype), to_f64(vr, pool.dtype)
+        kf, vf = pool.gather_head_f64(table, ctx_len, g)
         for i in range(q_len):
             last = ctx_len - q_len + i
             rows = qf[i, g * G:(g + 1) * G, :]
@@ -79,9 +84,10 @@ def attention_paged_seq(q, pool: HostPool, table, ctx_len: int, q_len: int,
     return out
 
 
-def attention_paged(q, pool: HostPool, tables, ctx_lens, q_len: int, scale: float) -> np.ndarray:
+def attention_paged(q, pool: HostPool, tables, ctx_lens, q_len: int, scale: float,
+                    q_dtype: str = None) -> np.ndarray:
     """Batch form. q: [B][q_len][H_q][d]; tables: [B][MB] (int, -1 padded);
     ctx_lens: [B]. Returns float64 [B][q_len][H_q][d]."""
     B, _, Hq, _ = q.shape
-    return np.stack([attention_paged_seq(q[b], pool, tables[b], int(ctx_lens[b]), q_len, Hq, scale)
+    return np.stack([attention_paged_seq(q[b], pool, tables[b], int(ctx_lens[b]), q_len, Hq, scale, q_dtype)
                      for b in range(B)])

@@ -26,7 +26,8 @@ def build_pool(w: Workload, shared_prefix: bool = True, fill_nan: bool = True):
     cfg = w.cfg
     B, MB = cfg.batch, w.max_blocks
     model = BlockPoolModel(w.num_blocks, cfg.block_size, w.free_order)
-    pool = HostPool(w.num_blocks, cfg.block_size, cfg.num_kv_heads, cfg.head_dim, cfg.dtype, fill_nan)
+    pool = HostPool(w.num_blocks, cfg.block_size, cfg.num_kv_heads, cfg.head_dim, cfg.kv_dtype or cfg.dtype,
+                    fill_nan)
     tables = [[-1] * MB for _ in range(B)]
     live = [0] * B
     if cfg.prefix_len and shared_prefix:

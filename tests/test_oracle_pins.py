@@ -109,10 +109,12 @@ def test_oracle_vs_brute_force(dtype, q_len, hq, hkv, d, bs, lens):
 
 # -- torch's fp64 scaled_dot_product_attention on the never-paged K/V ------
 
-def torch_sdpa_seq(q, k, v, q_len, G, scale, dtype):
+def torch_sdpa_seq(q, k, v, q_len, G, scale, dtype, kv_dtype=None):
+    kvd = kv_dtype or dtype
+    conv = (lambda a: np.asarray(a, dtype=np.float64)) if kvd == "f64" else (lambda a: to_f64(a, kvd))
     qt = torch.from_numpy(to_f64(q, dtype)).permute(1, 0, 2)[None]          # [1,Hq,q,d]
-    kt = torch.from_numpy(to_f64(k, dtype)).permute(1, 0, 2).repeat_interleave(G, 0)[None]
-    vt = torch.from_numpy(to_f64(v, dtype)).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+    kt = torch.from_numpy(conv(k)).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+    vt = torch.from_numpy(conv(v)).permute(1, 0, 2).repeat_interleave(G, 0)[None]
     L = k.shape[0]
     mask = torch.ones(q_len, L, dtype=torch.bool).tril(diagonal=L - q_len)
     o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)

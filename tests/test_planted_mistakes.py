@@ -14,6 +14,8 @@ import oracle.store as ostore
 from oracle.numerics import to_f64
 from tests import test_oracle_pins as pins
 from tests import test_allocator_model as apins
+from tests import test_oracle_fp8 as fpins
+import oracle.fp8 as ofp8
 
 
 def run_pins():
@@ -30,6 +32,9 @@ def run_pins():
         "kvbytes": lambda: [pins.test_kv_bytes_closed_form(c) for c in
                             pins.json.load(open(pins.os.path.join(pins.GOLDEN, "kv_bytes.json")))["cases"]],
         "lifo": apins.test_initial_free_order_and_lifo_reuse,
+        "fp8_codec": fpins.test_decode_table_matches_torch_float8_e4m3fn,
+        "fp8_attention": lambda: fpins.test_fp8_pool_attention_vs_torch_sdpa(
+            "llama3_70b_decode_fp8", dict(batch=2, len_const=100)),
         "cow": apins.test_four_samples_share_prompt_then_copy_only_the_diverging_block,
     }
     failed = []
@@ -114,6 +119,9 @@ MUTANTS = {
     "merge_without_rescale": lambda mp: mp.setattr(osplit, "lse_merge", _merge_no_rescale),
     "kv_bytes_doubled": lambda mp: mp.setattr(okv, "kv_bytes_per_token", lambda L, H, d, e: 4 * L * H * d * e),
     "free_list_fifo": lambda mp: mp.setattr(apins, "BlockPoolModel", FifoPool),
+    "fp8_exponent_bias_8": lambda mp: mp.setattr(ofp8, "_TABLE", ofp8.e4m3_decode_table() / 2.0),
+    "fp8_scale_not_applied": lambda mp: mp.setattr(ofp8, "dequantize",
+                                                   lambda c, s: ofp8.e4m3_decode(c) * 1.0),
 }
 
 

@@ -39,7 +39,10 @@ class Config:
     num_kv_heads: int
     head_dim: int
     block_size: int
-    dtype: str                      # "f32" or "bf16"
+    dtype: str                      # "f32" or "bf16": queries, outputs, K/V as written
+    # K/V storage in the pool: "" = as dtype; "fp8" = OCP E4M3 codes with one
+    # scale per (token, KV head), quantised from the bf16 rows when written
+    kv_dtype: str = ""
     # context lengths: explicit list, constant, or integer-uniform [lo, hi]
     lens: Optional[tuple] = None
     len_const: int = 0
@@ -88,6 +91,11 @@ CONFIGS = {
                num_kv_heads=8, head_dim=128, block_size=32, dtype="bf16",
                len_const=131072, partition_tokens=512,
                key_outlier_frac=0.01, key_outlier_scale=8.0),
+        # the 70B-shaped layer with an FP8 KV cache (same seeds and values as
+        # llama3_70b_decode; the pool holds their E4M3 quantisation)
+        Config("llama3_70b_decode_fp8", 2, batch=64, q_len=1, num_q_heads=64,
+               num_kv_heads=8, head_dim=128, block_size=32, dtype="bf16",
+               len_const=8192, kv_dtype="fp8"),
     ]
 }
 
