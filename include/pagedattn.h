@@ -41,6 +41,19 @@
  *       K: (((b*H_kv + h)*(head_dim/32) + c/32)*block_size + t)*32 + c%32
  *       V: ((b*H_kv + h)*head_dim + c)*block_size + t
  *   - bf16 is IEEE bfloat16 stored as uint16; f32 is IEEE binary32.
+ *   - FP8 pools (PA_DTYPE_FP8_E4M3; the pages name FP8 KV quantisation as the
+ *     capacity lever: Blog #54 section 4, Part 8 quantisation section) hold
+ *     OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ *     largest finite 448) plus one fp32 scale per (token, KV head); the value
+ *     of a code is decode(code) * scale. Each buffer is the codes followed by
+ *     the scales, pa_pool_buffer_bytes long:
+ *       k_pool: codes [num_blocks][num_kv_heads][head_dim/64][block_size][64],
+ *               then scales [num_blocks][num_kv_heads][block_size]
+ *       v_pool: codes [num_blocks][num_kv_heads][head_dim][block_size],
+ *               then scales [num_blocks][num_kv_heads][block_size]
+ *     Rows are written as bf16 and quantised per (token, KV head):
+ *     scale = max|x| / 448 (1 for an all-zero row), code = round-to-nearest-
+ *     even(x / scale), both in fp32.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -62,7 +75,10 @@ enum {
   PA_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
 };
 
-enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
+enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1, PA_DTYPE_FP8_E4M3 = 2 };
+
+/* K/V storage of the pools read by pa_attention (pa_attn_desc.kv_format). */
+enum { PA_KV_SAME = 0, PA_KV_FP8_E4M3 = 1 };
 
 /* Kernel selection for pa_attention. AUTO picks by dtype and row count. */
 enum { PA_PATH_AUTO = 0, PA_PATH_VALU = 1, PA_PATH_MFMA = 2 };
@@ -91,7 +107,8 @@ typedef struct pa_pool pa_pool;
  * initial order is initial_free_order[0..num_blocks) (host, a permutation of
  * 0..num_blocks-1; the first entry is handed out first), or ascending ids
  * when NULL. block_size must be 16 or 32, head_dim 64 or 128, dtype
- * PA_DTYPE_F32 or PA_DTYPE_BF16 (PA_ERR_UNSUPPORTED otherwise). The device
+ * PA_DTYPE_F32, PA_DTYPE_BF16 or PA_DTYPE_FP8_E4M3 (PA_ERR_UNSUPPORTED
+ * otherwise). The device
  * arrays k_pool/v_pool are not allocated here: the caller owns them.
  * *out receives the handle (PA_ERR_INVALID_ARG if out is NULL or the order
  * is not a permutation). [Blog #54 question 2: the free block pool] */
@@ -101,6 +118,12 @@ pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, int32_t num_kv_
 
 /* Release the handle (NULL is a no-op). Device memory is not touched. */
 void pa_pool_destroy(pa_pool* pool);
+
+/* Bytes of one pool buffer (k_pool or v_pool; both have this size) for the
+ * given shape and storage dtype, scales included for FP8. -1 for an invalid
+ * or unsupported shape. */
+int64_t pa_pool_buffer_bytes(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t dtype);
 
 /* Bytes of K plus V that one token occupies: 2 * num_layers * num_kv_heads *
  * head_dim * elem_bytes; at 16-bit storage this is 4 * L * H_kv * d_k
@@ -171,7 +194,8 @@ pa_status pa_write_kv(pa_pool* pool, void* k_pool, void* v_pool, int32_t* block_
                       int32_t table_capacity, int32_t* num_blocks_inout, int32_t start_pos,
                       int32_t n_tokens, const void* k_new, const void* v_new, void* stream);
 
-/* Copy whole physical blocks (every KV head, K and V) on `stream`:
+/* Copy whole physical blocks (every KV head, K and V, and their scales in an
+ * FP8 pool) on `stream`:
  * block src_dst[2k] -> block src_dst[2k+1] for k < n_pairs (host array).
  * The device half of copy-on-write. PA_ERR_INVALID_ARG for an id out of
  * range or src == dst. */
@@ -202,7 +226,9 @@ typedef struct pa_attn_desc {
                                  physical block is read by one sequence only, so K/V
                                  loads stream past the caches; 1 = some blocks are
                                  shared (a common prompt), so K/V loads stay cacheable */
-  int32_t reserved[3];        /* must be 0 */
+  int32_t kv_format;          /* PA_KV_SAME: pools in dtype; PA_KV_FP8_E4M3: FP8 pools
+                                 (dtype must be PA_DTYPE_BF16, MFMA path only) */
+  int32_t reserved[2];        /* must be 0 */
 } pa_attn_desc;
 
 /* What pa_attention launches for a descriptor (for tests and profiling). */

@@ -43,10 +43,11 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndar
 
 
 def attention_contiguous(q, k, v, q_len: int, num_q_heads: int, num_kv_heads: int,
-                         scale: float, dtype: str) -> np.ndarray:
+                         scale: float, dtype: str, kv_dtype: str = None) -> np.ndarray:
     """One sequence with contiguous K/V.
 
-    q: [q_len][H_q][d]; k, v: [L][H_kv][d] in storage format.
+    q: [q_len][H_q][d]; k, v: [L][H_kv][d] in storage format (kv_dtype, default
+    dtype; "f64" for values already in float64, e.g. dequantised FP8).
     Returns float64 [q_len][H_q][d].
     """
     G = num_q_heads // num_kv_heads
@@ -54,8 +55,8 @@ def attention_contiguous(q, k, v, q_len: int, num_q_heads: int, num_kv_heads: in
     qf = to_f64(q, dtype)
     out = np.empty(qf.shape, dtype=np.float64)
     for g in range(num_kv_heads):
-        kf = to_f64(k[:, g, :], dtype)
-        vf = to_f64(v[:, g, :], dtype)
+        kf = to_f64(k[:, g, :], kv_dtype or dtype)
+        vf = to_f64(v[:, g, :], kv_dtype or dtype)
         for i in range(q_len):
             last = L - q_len + i                      # row i sees 0..last
             rows = qf[i, g * G:(g + 1) * G, :]        # the G query heads of KV head g

@@ -5,6 +5,8 @@ import numpy as np
 def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
     """Storage values -> float64. bf16 bit patterns widen exactly: the 16 bits
     become the high half of an IEEE float32, which float64 holds exactly."""
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":

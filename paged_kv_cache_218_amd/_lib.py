@@ -11,7 +11,8 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_NO_FREE_BLOCK, PA_ERR_BAD_BLOCK, PA_ERR_HIP = range(6)
-PA_DTYPE_F32, PA_DTYPE_BF16 = 0, 1
+PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3 = 0, 1, 2
+PA_KV_SAME, PA_KV_FP8_E4M3 = 0, 1
 PA_PATH_AUTO, PA_PATH_VALU, PA_PATH_MFMA = 0, 1, 2
 PA_SCHED_PARTITIONS, PA_SCHED_BALANCED = 0, 1
 
@@ -24,7 +25,7 @@ class AttnDesc(C.Structure):
                 ("head_dim", i32), ("block_size", i32), ("max_blocks_per_seq", i32),
                 ("num_blocks", i32), ("dtype", i32), ("max_context", i32), ("path", i32),
                 ("partition_tokens", i32), ("waves_per_group", i32), ("kv_shared", i32),
-                ("reserved", i32 * 3)]
+                ("kv_format", i32), ("reserved", i32 * 2)]
 
 
 class AttnPlan(C.Structure):
@@ -39,6 +40,7 @@ SIGNATURES = [
     ("pa_pool_create", i32, [i32, i32, i32, i32, i32, pi32, C.POINTER(vp)]),
     ("pa_pool_destroy", None, [vp]),
     ("pa_kv_bytes_per_token", i64, [i32, i32, i32, i32]),
+    ("pa_pool_buffer_bytes", i64, [i32, i32, i32, i32, i32]),
     ("pa_block_alloc", i32, [vp, pi32]),
     ("pa_block_fork", i32, [vp, i32]),
     ("pa_block_free", i32, [vp, i32]),

@@ -85,6 +85,10 @@ def pa_kv_bytes_per_token(num_layers, num_kv_heads, head_dim, elem_bytes) -> int
     return lib.pa_kv_bytes_per_token(num_layers, num_kv_heads, head_dim, elem_bytes)
 
 
+def pa_pool_buffer_bytes(num_blocks, block_size, num_kv_heads, head_dim, dtype) -> int:
+    return lib.pa_pool_buffer_bytes(num_blocks, block_size, num_kv_heads, head_dim, dtype)
+
+
 def pa_block_alloc(pool: Pool) -> int:
     b = C.c_int32()
     _check(lib.pa_block_alloc(pool.handle, C.byref(b)), "pa_block_alloc")
@@ -154,13 +158,13 @@ def pa_copy_blocks(pool: Pool, k_pool, v_pool, src_dst: np.ndarray, stream=None)
 
 def make_desc(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
               dtype, max_context, path=_lib.PA_PATH_AUTO, partition_tokens=0, waves_per_group=0,
-              kv_shared=0) -> AttnDesc:
+              kv_shared=0, kv_format=_lib.PA_KV_SAME) -> AttnDesc:
     d = AttnDesc()
     d.num_seqs, d.num_q_heads, d.num_kv_heads = num_seqs, num_q_heads, num_kv_heads
     d.head_dim, d.block_size, d.max_blocks_per_seq = head_dim, block_size, max_blocks_per_seq
     d.num_blocks, d.dtype, d.max_context = num_blocks, dtype, max_context
     d.path, d.partition_tokens, d.waves_per_group = path, partition_tokens, waves_per_group
-    d.kv_shared = kv_shared
+    d.kv_shared, d.kv_format = kv_shared, kv_format
     return d
 
 

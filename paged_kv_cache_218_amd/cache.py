@@ -1,7 +1,8 @@
 """A batch of sequences over one paged KV pool, driven through the C ABI.
 
 Holds the pool handle (host refcounts and free list), the device K/V pools
-(torch tensors, pool layout k [NB][H_kv][d/32][bs][32], v [NB][H_kv][d][bs]), the
+(torch tensors, pool layout k [NB][H_kv][d/32][bs][32], v [NB][H_kv][d][bs];
+FP8 pools are byte buffers of E4M3 codes followed by fp32 scales), the
 host block tables and each sequence's live-block count. Every operation is
 one ``pa_*`` call; torch only provides the device memory and the stream.
 """
@@ -28,18 +29,32 @@ def _to_device(arr: np.ndarray, torch_dtype, device):
 class PagedKVCache:
     def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, torch_dtype,
                  num_seqs: int, max_blocks: int, initial_free_order=None, device="cuda",
-                 fill_nan: bool = True):
+                 fill_nan: bool = True, kv_fp8: bool = False):
+        """torch_dtype: the dtype of queries, outputs and written K/V rows;
+        kv_fp8: the pools store E4M3 codes plus scales (rows written as bf16)."""
         import torch
         self.nb, self.bs, self.hkv, self.d = num_blocks, block_size, num_kv_heads, head_dim
         self.torch_dtype, self.device = torch_dtype, device
         self.dtype = api.dtype_code(torch_dtype)
-        self.pool = api.pa_pool_create(num_blocks, block_size, num_kv_heads, head_dim, self.dtype,
+        self.kv_fp8 = kv_fp8
+        pool_dtype = _lib.PA_DTYPE_FP8_E4M3 if kv_fp8 else self.dtype
+        self.pool = api.pa_pool_create(num_blocks, block_size, num_kv_heads, head_dim, pool_dtype,
                                        initial_free_order)
-        fill = float("nan") if fill_nan else 0.0
-        self.k_pool = torch.full((num_blocks, num_kv_heads, head_dim // 32, block_size, 32), fill,
-                                 dtype=torch_dtype, device=device)
-        self.v_pool = torch.full((num_blocks, num_kv_heads, head_dim, block_size), fill,
-                                 dtype=torch_dtype, device=device)
+        if kv_fp8:
+            nbytes = api.pa_pool_buffer_bytes(num_blocks, block_size, num_kv_heads, head_dim, pool_dtype)
+            codes = num_blocks * num_kv_heads * block_size * head_dim
+            self.k_pool = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+            self.v_pool = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+            if fill_nan:   # the E4M3 NaN code, and NaN scales
+                for t in (self.k_pool, self.v_pool):
+                    t[:codes].fill_(0x7F)
+                    t[codes:].view(torch.float32).fill_(float("nan"))
+        else:
+            fill = float("nan") if fill_nan else 0.0
+            self.k_pool = torch.full((num_blocks, num_kv_heads, head_dim // 32, block_size, 32), fill,
+                                     dtype=torch_dtype, device=device)
+            self.v_pool = torch.full((num_blocks, num_kv_heads, head_dim, block_size), fill,
+                                     dtype=torch_dtype, device=device)
         self.tables = np.full((num_seqs, max_blocks), -1, dtype=np.int32)
         self.live = [0] * num_seqs
         self.shared = False   # some block is (or was) in more than one table
@@ -74,7 +89,8 @@ class PagedKVCache:
              waves_per_group=0):
         return api.make_desc(self.tables.shape[0], num_q_heads, self.hkv, self.d, self.bs,
                              self.tables.shape[1], self.nb, self.dtype, max_context, path, partition_tokens,
-                             waves_per_group, int(self.shared))
+                             waves_per_group, int(self.shared),
+                             _lib.PA_KV_FP8_E4M3 if self.kv_fp8 else _lib.PA_KV_SAME)
 
     def attention(self, q, tables_dev, lens_dev, q_len: int, scale: float, max_context: int,
                   path=_lib.PA_PATH_AUTO, partition_tokens=0, waves_per_group=0, out=None, workspace=None,
@@ -110,7 +126,7 @@ class PagedKVCache:
         cfg = w.cfg
         tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
         c = cls(w.num_blocks, cfg.block_size, cfg.num_kv_heads, cfg.head_dim, tdt, cfg.batch,
-                w.max_blocks, w.free_order, device, fill_nan)
+                w.max_blocks, w.free_order, device, fill_nan, kv_fp8=cfg.kv_dtype == "fp8")
         if cfg.prefix_len:
             pk, pv = _to_device(w.prefix_k, tdt, device), _to_device(w.prefix_v, tdt, device)
             if shared_prefix:

@@ -64,6 +64,8 @@ struct AttnArgs {
   float* part_ml;  // partitions: [rows_total][P][2]; balanced: [pieces][R][2] (m base-2, l)
   float* part_o;   // partitions: [rows_total][P][d]; balanced: [pieces][R][d]
   int32_t* counters;  // balanced: arrival count per segment, zero between calls
+  const float* k_scales;  // FP8 pools: per (block, head, slot) scales after the codes
+  const float* v_scales;
   int32_t num_seqs, hq, hkv, group, mb, nb, q_len, max_ctx, parts, part_tokens;
   float scale_log2;  // scale * log2(e)
 };
@@ -199,12 +201,46 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   else return *reinterpret_cast<const u32x4*>(p);
 }
 
+template <bool STREAM>
+__device__ __forceinline__ u32x4 load16(const uint8_t* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
+}
+template <bool STREAM>
+__device__ __forceinline__ u32x2 load8(const uint8_t* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  else return *reinterpret_cast<const u32x2*>(p);
+}
+template <bool STREAM>
+__device__ __forceinline__ f32x4 load16f(const float* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  else return *reinterpret_cast<const f32x4*>(p);
+}
+
+// two E4M3 codes (the low or high 16 bits of w) -> two bf16, exactly
+template <bool HIGH>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w), 1.0f, HIGH));
+}
+
 template <int D>
 struct StepBuf {
   u32x4 k[2][D / 32];  // two 16-token K tiles, D/32 k-steps each
   u32x4 v[D / 16];     // V^T head-dim tiles
   int tb;              // first token of the step
   bool ok;             // block ids in range
+};
+
+// FP8 pools: 16 K codes per lane per 64-element slab (two MFMA k-steps), 8 V
+// codes per lane per head-dim tile, and the K and V scales of the lane's 8
+// tokens (8j .. 8j+7 of the step).
+template <int D>
+struct StepBuf8 {
+  u32x4 k[2][D / 64];
+  u32x2 v[D / 16];
+  f32x4 ks[2], vs[2];
+  int tb;
+  bool ok;
 };
 
 // Online-softmax state of one wavefront: lane (n, j) holds row 16*nt + n,
@@ -231,7 +267,7 @@ __device__ __forceinline__ void wave_state_init(WaveState<D, NT>& st) {
 // One wavefront's share of a piece: steps first, first+W, ... < end of
 // sequence b (context L), KV head g. Every step covers 32 tokens; tokens at
 // or past L, and tokens after a row's causal limit, are masked.
-template <int D, int BS, int NT, bool STREAM>
+template <int D, int BS, int NT, bool STREAM, bool KV8>
 __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int first, int end, int W,
                                 WaveState<D, NT>& st) {
   constexpr int KS = D / 32;  // k-steps over the head dim for QK
@@ -246,7 +282,10 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
   const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v_pool);
   const int32_t* __restrict__ table = a.tables + int64_t(b) * a.mb;
 
-  // query rows as the B operand of QK, per 16-row tile and k-step
+  // query rows as the B operand of QK, per 16-row tile and k-step. The k
+  // elements of lane j in k-step ks: d = 32ks + 8j .. +7 (bf16 pools), or
+  // d = 64(ks/2) + 16j + 8(ks%2) .. +7 (FP8 pools, where one 16-byte load
+  // holds two k-steps of a token's 64-element slab)
   u32x4 qop[NT][KS];
   int lim[NT];  // last visible position of this lane's row
 #pragma unroll
@@ -258,134 +297,284 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
       u32x4 v = {0, 0, 0, 0};
       if (r < R) {
         const int i = r / a.group, h = g * a.group + r % a.group;
-        v = *reinterpret_cast<const u32x4*>(q + (int64_t(b * a.q_len + i) * a.hq + h) * D + 32 * ks + 8 * j);
+        const int d0 = KV8 ? 64 * (ks >> 1) + 16 * j + 8 * (ks & 1) : 32 * ks + 8 * j;
+        v = *reinterpret_cast<const u32x4*>(q + (int64_t(b * a.q_len + i) * a.hq + h) * D + d0);
       }
       qop[nt][ks] = v;
     }
   }
 
-  const int64_t head_stride = int64_t(BS) * D;  // elements of one (block, head) slice
-
-  // Issue the loads of one 32-token step into a register buffer. The
-  // physical block ids are scalar (wave-uniform) loads from the table.
-  auto load_step = [&](StepBuf<D>& buf, int step) {
-    const int tb = kStep * step;
-    buf.tb = tb;
-    const int blk0 = table[tb / BS];
-    const bool have1 = BS == 32 || tb + 16 < L;
-    const int blk1 = (BS == 16 && have1) ? table[tb / BS + 1] : blk0;
-    buf.ok = blk0 >= 0 && blk0 < a.nb && blk1 >= 0 && blk1 < a.nb;
-    const int64_t o0 = buf.ok ? (int64_t(blk0) * a.hkv + g) * head_stride : 0;
-    const int64_t o1 = buf.ok ? (int64_t(blk1) * a.hkv + g) * head_stride : 0;
-    // K tiles: A operand, token of row n in tile i. K slab ks holds head-dim
-    // elements 32ks..32ks+31 of the block's tokens back to back (64 B each),
-    // so one load instruction reads tokens {0-3, 8-11, 16-19, 24-27} (tile 0)
-    // or {4-7, ...} (tile 1) of slab ks: four runs of 256 contiguous bytes.
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tok = 8 * (n >> 2) + 4 * i + (n & 3);
-      const bool second = BS == 16 && tok >= 16;
-      const uint16_t* row = kp + (second ? o1 : o0) + (tok & (BS - 1)) * 32 + 8 * j;
-      const bool ok = buf.ok && (!second || have1);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4 v = {0, 0, 0, 0};
-        if (ok) v = load16<STREAM>(row + ks * (BS * 32));
-        buf.k[i][ks] = v;
-      }
-    }
-    // V^T slices: A operand of PV, head-dim row 16*dt + n, tokens 8j..8j+7
-    {
-      const bool second = BS == 16 && j >= 2;
-      const uint16_t* base = vp + (second ? o1 : o0) + (BS == 32 ? 8 * j : 8 * (j & 1)) + n * BS;
-      const bool ok = buf.ok && (!second || have1);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        u32x4 v = {0, 0, 0, 0};
-        if (ok) v = load16<STREAM>(base + 16 * dt * BS);
-        buf.v[dt] = v;
-      }
-    }
-  };
-
-  // Scores, online softmax and P.V of one loaded step.
-  auto compute_step = [&](StepBuf<D>& buf) {
-    const int tb = buf.tb;
-    if (!buf.ok) {
-      st.poisoned = true;
-      return;
-    }
-    // tail step: zero V entries past the context so 0 * NaN never reaches the sum
-    if (tb + kStep > L) {
-      const int valid = min(max(L - (tb + 8 * j), 0), 8);  // tokens of this lane's 8 still valid
-#pragma unroll
-      for (int w4 = 0; w4 < 4; ++w4) {
-        const uint32_t keep = (2 * w4 + 1 < valid) ? 0xffffffffu : (2 * w4 < valid ? 0x0000ffffu : 0u);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) buf.v[dt][w4] &= keep;
-      }
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 sc[2];
+  if constexpr (KV8) {
+    const uint8_t* __restrict__ kc = static_cast<const uint8_t*>(a.k_pool);
+    const uint8_t* __restrict__ vc = static_cast<const uint8_t*>(a.v_pool);
+    const int64_t slice = int64_t(BS) * D;  // bytes of one (block, head) code slice
+    auto load_step8 = [&](StepBuf8<D>& buf, int step) {
+      const int tb = kStep * step;
+      buf.tb = tb;
+      const int blk0 = table[tb / BS];
+      const bool have1 = BS == 32 || tb + 16 < L;
+      const int blk1 = (BS == 16 && have1) ? table[tb / BS + 1] : blk0;
+      buf.ok = blk0 >= 0 && blk0 < a.nb && blk1 >= 0 && blk1 < a.nb;
+      const int64_t s0 = buf.ok ? int64_t(blk0) * a.hkv + g : 0;  // slice index
+      const int64_t s1 = buf.ok ? int64_t(blk1) * a.hkv + g : 0;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        sc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        const int tok = 8 * (n >> 2) + 4 * i + (n & 3);
+        const bool second = BS == 16 && tok >= 16;
+        const uint8_t* row = kc + (second ? s1 : s0) * slice + (tok & (BS - 1)) * 64 + 16 * j;
+        const bool ok = buf.ok && (!second || have1);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          sc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf.k[i][ks]),
-                                                           __builtin_bit_cast(bf16x8, qop[nt][ks]),
-                                                           sc[i], 0, 0, 0);
+        for (int sl = 0; sl < D / 64; ++sl) {
+          u32x4 v = {0, 0, 0, 0};
+          if (ok) v = load16<STREAM>(row + sl * (BS * 64));
+          buf.k[i][sl] = v;
+        }
       }
-      // mask and scale; e = 4*i + r is token tb + 8j + e
-      float s2[8];
-      float mx = -INFINITY;
+      const bool second = BS == 16 && j >= 2;
+      const bool ok = buf.ok && (!second || have1);
+      const int toff = BS == 32 ? 8 * j : 8 * (j & 1);  // the lane's 8 tokens within their block
+      const int64_t sl_idx = second ? s1 : s0;
+      const uint8_t* base = vc + sl_idx * slice + toff + n * BS;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        u32x2 v = {0, 0};
+        if (ok) v = load8<STREAM>(base + 16 * dt * BS);
+        buf.v[dt] = v;
+      }
+      const f32x4 one = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        buf.ks[h] = ok ? load16f<STREAM>(a.k_scales + sl_idx * BS + toff + 4 * h) : one;
+        buf.vs[h] = ok ? load16f<STREAM>(a.v_scales + sl_idx * BS + toff + 4 * h) : one;
+      }
+    };
+    auto compute_step8 = [&](StepBuf8<D>& buf) {
+      const int tb = buf.tb;
+      if (!buf.ok) {
+        st.poisoned = true;
+        return;
+      }
+      // codes -> bf16 (exact); K: slab sl gives k-steps 2sl (codes 0-7) and 2sl+1 (8-15)
+      u32x4 kop[2][KS];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tok = tb + 8 * j + 4 * i + r;
-          const bool vis = tok < L && tok <= lim[nt];
-          const float v = vis ? sc[i][r] * a.scale_log2 : -INFINITY;
-          s2[4 * i + r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(st.m[nt], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(st.m[nt] - m_use);
-      st.m[nt] = m_new;
-      uint32_t pk[4];
-      float psum = 0.f;
+        for (int sl = 0; sl < D / 64; ++sl)
 #pragma unroll
-      for (int w4 = 0; w4 < 4; ++w4) {
-        const float p0 = fast_exp2(s2[2 * w4] - m_use);
-        const float p1 = fast_exp2(s2[2 * w4 + 1] - m_use);
-        const uint32_t packed = pack_bf16x2(p0, p1);
-        pk[w4] = packed;
-        // the sum uses the rounded weights, so the output stays a convex combination
-        psum += __uint_as_float(packed << 16) + __uint_as_float(packed & 0xffff0000u);
-      }
-      st.l[nt] = st.l[nt] * alpha + psum;
-      const u32x4 pop = {pk[0], pk[1], pk[2], pk[3]};
+          for (int hh = 0; hh < 2; ++hh) {
+            const uint32_t w0 = buf.k[i][sl][2 * hh], w1 = buf.k[i][sl][2 * hh + 1];
+            kop[i][2 * sl + hh] = (u32x4){fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                                          fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1)};
+          }
+      u32x4 vop[DT];
+      const int valid = min(max(L - (tb + 8 * j), 0), 8);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        st.acc[nt][dt] *= alpha;
-        st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf.v[dt]),
-                                                                 __builtin_bit_cast(bf16x8, pop),
-                                                                 st.acc[nt][dt], 0, 0, 0);
+        const uint32_t w0 = buf.v[dt][0], w1 = buf.v[dt][1];
+        vop[dt] = (u32x4){fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                          fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1)};
       }
+      if (tb + kStep > L) {  // tail: tokens past the context hold the NaN code
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          const uint32_t keep = (2 * w4 + 1 < valid) ? 0xffffffffu : (2 * w4 < valid ? 0x0000ffffu : 0u);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) vop[dt][w4] &= keep;
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x4 sc[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          sc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            sc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[i][ks]),
+                                                             __builtin_bit_cast(bf16x8, qop[nt][ks]),
+                                                             sc[i], 0, 0, 0);
+        }
+        // each token's K scale multiplies its score; e = 4i + r is token tb + 8j + e
+        float s2[8];
+        bool vis[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = 4 * i + r, tok = tb + 8 * j + e;
+            vis[e] = tok < L && tok <= lim[nt];
+            const float v = vis[e] ? sc[i][r] * buf.ks[i][r] * a.scale_log2 : -INFINITY;
+            s2[e] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(st.m[nt], mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2(st.m[nt] - m_use);
+        st.m[nt] = m_new;
+        // Each token's V scale multiplies its weight in P.V (not in the row
+        // sum). The scaled weight w is not a bf16 number, so it enters P.V as
+        // w_hi + w_lo, two bf16 parts (residual ~2^-17 relative): one
+        // dominant token would otherwise carry w's 2^-9 rounding into the row.
+        uint32_t pk_hi[4], pk_lo[4];
+        float psum = 0.f;
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          const int e0 = 2 * w4, e1 = 2 * w4 + 1;
+          const float p0 = fast_exp2(s2[e0] - m_use), p1 = fast_exp2(s2[e1] - m_use);
+          psum += p0 + p1;
+          const float q0 = vis[e0] ? p0 * buf.vs[e0 / 4][e0 % 4] : 0.f;
+          const float q1 = vis[e1] ? p1 * buf.vs[e1 / 4][e1 % 4] : 0.f;
+          const uint32_t hi = pack_bf16x2(q0, q1);
+          pk_hi[w4] = hi;
+          pk_lo[w4] = pack_bf16x2(q0 - __uint_as_float(hi << 16), q1 - __uint_as_float(hi & 0xffff0000u));
+        }
+        st.l[nt] = st.l[nt] * alpha + psum;
+        const u32x4 pop_hi = {pk_hi[0], pk_hi[1], pk_hi[2], pk_hi[3]};
+        const u32x4 pop_lo = {pk_lo[0], pk_lo[1], pk_lo[2], pk_lo[3]};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          st.acc[nt][dt] *= alpha;
+          st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[dt]),
+                                                                   __builtin_bit_cast(bf16x8, pop_hi),
+                                                                   st.acc[nt][dt], 0, 0, 0);
+          st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[dt]),
+                                                                   __builtin_bit_cast(bf16x8, pop_lo),
+                                                                   st.acc[nt][dt], 0, 0, 0);
+        }
+      }
+    };
+    StepBuf8<D> buf;
+    for (int s = first; s < end; s += W) {
+      load_step8(buf, s);
+      compute_step8(buf);
     }
-  };
-
-  // One step buffer per wave: the other waves on the SIMD (three per SIMD
-  // fit) hide this wave's load latency. (A two-buffer ping-pong was measured
-  // no faster: the extra registers cost a wave per SIMD.)
-  StepBuf<D> buf;
-  for (int s = first; s < end; s += W) {
-    load_step(buf, s);
-    compute_step(buf);
+  } else {
+  const int64_t head_stride = int64_t(BS) * D;  // elements of one (block, head) slice
+  
+    // Issue the loads of one 32-token step into a register buffer. The
+    // physical block ids are scalar (wave-uniform) loads from the table.
+    auto load_step = [&](StepBuf<D>& buf, int step) {
+      const int tb = kStep * step;
+      buf.tb = tb;
+      const int blk0 = table[tb / BS];
+      const bool have1 = BS == 32 || tb + 16 < L;
+      const int blk1 = (BS == 16 && have1) ? table[tb / BS + 1] : blk0;
+      buf.ok = blk0 >= 0 && blk0 < a.nb && blk1 >= 0 && blk1 < a.nb;
+      const int64_t o0 = buf.ok ? (int64_t(blk0) * a.hkv + g) * head_stride : 0;
+      const int64_t o1 = buf.ok ? (int64_t(blk1) * a.hkv + g) * head_stride : 0;
+      // K tiles: A operand, token of row n in tile i. K slab ks holds head-dim
+      // elements 32ks..32ks+31 of the block's tokens back to back (64 B each),
+      // so one load instruction reads tokens {0-3, 8-11, 16-19, 24-27} (tile 0)
+      // or {4-7, ...} (tile 1) of slab ks: four runs of 256 contiguous bytes.
+  #pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int tok = 8 * (n >> 2) + 4 * i + (n & 3);
+        const bool second = BS == 16 && tok >= 16;
+        const uint16_t* row = kp + (second ? o1 : o0) + (tok & (BS - 1)) * 32 + 8 * j;
+        const bool ok = buf.ok && (!second || have1);
+  #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4 v = {0, 0, 0, 0};
+          if (ok) v = load16<STREAM>(row + ks * (BS * 32));
+          buf.k[i][ks] = v;
+        }
+      }
+      // V^T slices: A operand of PV, head-dim row 16*dt + n, tokens 8j..8j+7
+      {
+        const bool second = BS == 16 && j >= 2;
+        const uint16_t* base = vp + (second ? o1 : o0) + (BS == 32 ? 8 * j : 8 * (j & 1)) + n * BS;
+        const bool ok = buf.ok && (!second || have1);
+  #pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          u32x4 v = {0, 0, 0, 0};
+          if (ok) v = load16<STREAM>(base + 16 * dt * BS);
+          buf.v[dt] = v;
+        }
+      }
+    };
+  
+    // Scores, online softmax and P.V of one loaded step.
+    auto compute_step = [&](StepBuf<D>& buf) {
+      const int tb = buf.tb;
+      if (!buf.ok) {
+        st.poisoned = true;
+        return;
+      }
+      // tail step: zero V entries past the context so 0 * NaN never reaches the sum
+      if (tb + kStep > L) {
+        const int valid = min(max(L - (tb + 8 * j), 0), 8);  // tokens of this lane's 8 still valid
+  #pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          const uint32_t keep = (2 * w4 + 1 < valid) ? 0xffffffffu : (2 * w4 < valid ? 0x0000ffffu : 0u);
+  #pragma unroll
+          for (int dt = 0; dt < DT; ++dt) buf.v[dt][w4] &= keep;
+        }
+      }
+  #pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x4 sc[2];
+  #pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          sc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            sc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf.k[i][ks]),
+                                                             __builtin_bit_cast(bf16x8, qop[nt][ks]),
+                                                             sc[i], 0, 0, 0);
+        }
+        // mask and scale; e = 4*i + r is token tb + 8j + e
+        float s2[8];
+        float mx = -INFINITY;
+  #pragma unroll
+        for (int i = 0; i < 2; ++i)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tok = tb + 8 * j + 4 * i + r;
+            const bool vis = tok < L && tok <= lim[nt];
+            const float v = vis ? sc[i][r] * a.scale_log2 : -INFINITY;
+            s2[4 * i + r] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(st.m[nt], mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2(st.m[nt] - m_use);
+        st.m[nt] = m_new;
+        uint32_t pk[4];
+        float psum = 0.f;
+  #pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          const float p0 = fast_exp2(s2[2 * w4] - m_use);
+          const float p1 = fast_exp2(s2[2 * w4 + 1] - m_use);
+          const uint32_t packed = pack_bf16x2(p0, p1);
+          pk[w4] = packed;
+          // the sum uses the rounded weights, so the output stays a convex combination
+          psum += __uint_as_float(packed << 16) + __uint_as_float(packed & 0xffff0000u);
+        }
+        st.l[nt] = st.l[nt] * alpha + psum;
+        const u32x4 pop = {pk[0], pk[1], pk[2], pk[3]};
+  #pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          st.acc[nt][dt] *= alpha;
+          st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf.v[dt]),
+                                                                   __builtin_bit_cast(bf16x8, pop),
+                                                                   st.acc[nt][dt], 0, 0, 0);
+        }
+      }
+    };
+  
+    // One step buffer per wave: the other waves on the SIMD (three per SIMD
+    // fit) hide this wave's load latency. (A two-buffer ping-pong was measured
+    // no faster: the extra registers cost a wave per SIMD.)
+    StepBuf<D> buf;
+    for (int s = first; s < end; s += W) {
+      load_step(buf, s);
+      compute_step(buf);
+    }
   }
 }
 
@@ -443,7 +632,7 @@ __device__ __forceinline__ void combine_waves(const float* smem, int W, int R, i
 
 // Fixed partitions: workgroup = (sequence, KV head, partition); partitions
 // that do not cover the whole sequence leave partials for lse_merge.
-template <int D, int BS, int NT, bool STREAM>
+template <int D, int BS, int NT, bool STREAM, bool KV8>
 __global__ __launch_bounds__(256, 2) void mfma_attn(AttnArgs a) {
   extern __shared__ float smem[];
   const int W = blockDim.x / 64, wave = threadIdx.x / 64;
@@ -454,7 +643,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn(AttnArgs a) {
   WaveState<D, NT> st;
   wave_state_init(st);
   const int s0 = t.t0 / kStep, s1 = (t.t1 + kStep - 1) / kStep;
-  mfma_wave_steps<D, BS, NT, STREAM>(a, t.b, t.g, t.L, s0 + wave, s1, W, st);
+  mfma_wave_steps<D, BS, NT, STREAM, KV8>(a, t.b, t.g, t.L, s0 + wave, s1, W, st);
   const bool bad = park_states(st, R, smem);
   merge_and_store<uint16_t, D>(a, t, R, R, W, smem, smem + W * R, smem + 2 * W * R, bad);
 }
@@ -477,7 +666,7 @@ __device__ __forceinline__ int64_t owner(int64_t x, int64_t S, int64_t N) {
   return k;
 }
 
-template <int D, int BS, int NT, bool STREAM>
+template <int D, int BS, int NT, bool STREAM, bool KV8>
 __global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
   extern __shared__ float smem[];  // [B+1] step prefix sums, then the parked states
   const int W = blockDim.x / 64, wave = threadIdx.x / 64;
@@ -552,7 +741,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
     const int L = a.lens[b];
     WaveState<D, NT> st;
     wave_state_init(st);
-    mfma_wave_steps<D, BS, NT, STREAM>(a, b, g, L, first + wave, last, W, st);
+    mfma_wave_steps<D, BS, NT, STREAM, KV8>(a, b, g, L, first + wave, last, W, st);
     const bool bad = park_states(st, R, park);
     const int64_t seg = int64_t(b) * a.hkv + g;
     const bool whole = first == 0 && last == nb;
@@ -935,6 +1124,7 @@ __global__ __launch_bounds__(256) void lse_merge(AttnArgs a) {
 struct Plan {
   int path, sched, part_tokens, parts, waves, grid, merge_grid, nt, rows;
   bool stream;  // K/V loads with the non-temporal hint
+  bool kv8;     // FP8 pools
   int64_t segments, pieces;  // balanced schedule: segments, partial slots
   size_t ws;
 };
@@ -946,9 +1136,10 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   if (!d || !pl) return PA_ERR_INVALID_ARG;
-  for (int k = 0; k < 3; ++k)
+  for (int k = 0; k < 2; ++k)
     if (d->reserved[k] != 0) return PA_ERR_INVALID_ARG;
   if (d->kv_shared != 0 && d->kv_shared != 1) return PA_ERR_INVALID_ARG;
+  if (d->kv_format != PA_KV_SAME && d->kv_format != PA_KV_FP8_E4M3) return PA_ERR_INVALID_ARG;
   if (d->waves_per_group != 0 && d->waves_per_group != 1 && d->waves_per_group != 2 &&
       d->waves_per_group != 4)
     return PA_ERR_INVALID_ARG;
@@ -973,9 +1164,11 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
     if (d->dtype != PA_DTYPE_BF16 || rows > kMfmaMaxRows) return PA_ERR_UNSUPPORTED;
   } else if (path == PA_PATH_VALU) {
     if (rows > kValuMaxRows) return PA_ERR_UNSUPPORTED;
+    if (d->kv_format == PA_KV_FP8_E4M3) return PA_ERR_UNSUPPORTED;  // FP8 pools: MFMA path only
   } else {
     return PA_ERR_INVALID_ARG;
   }
+  if (d->kv_format == PA_KV_FP8_E4M3 && d->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
   const int waves = d->waves_per_group ? d->waves_per_group : 4;
   const int64_t pairs = int64_t(d->num_seqs) * d->num_kv_heads;
   const int64_t out_rows = int64_t(d->num_seqs) * q_len * d->num_q_heads;
@@ -985,6 +1178,7 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   pl->nt = rows > 16 ? 2 : 1;
   pl->rows = int(rows);
   pl->stream = d->kv_shared == 0;
+  pl->kv8 = d->kv_format == PA_KV_FP8_E4M3;
   const bool balanced = path == PA_PATH_MFMA && d->partition_tokens == 0 &&
                         d->num_seqs <= kMaxBalancedSeqs;
   if (balanced) {
@@ -1053,22 +1247,22 @@ int resident_groups(const void* kernel, int threads, size_t lds) {
 }
 
 // The main kernel a plan launches (one template instance per shape).
+template <int D, int BS, int NT, bool STREAM, bool KV8>
+const void* mfma_kernel(bool balanced) {
+  return balanced ? reinterpret_cast<const void*>(mfma_attn_balanced<D, BS, NT, STREAM, KV8>)
+                  : reinterpret_cast<const void*>(mfma_attn<D, BS, NT, STREAM, KV8>);
+}
+
+template <int D, int BS, int NT>
+const void* mfma_kernel(const Plan& pl) {
+  const bool bal = pl.sched == PA_SCHED_BALANCED;
+  if (pl.kv8) return pl.stream ? mfma_kernel<D, BS, NT, true, true>(bal) : mfma_kernel<D, BS, NT, false, true>(bal);
+  return pl.stream ? mfma_kernel<D, BS, NT, true, false>(bal) : mfma_kernel<D, BS, NT, false, false>(bal);
+}
+
 template <int D, int BS>
 const void* main_kernel(const Plan& pl, int dtype) {
-  if (pl.path == PA_PATH_MFMA && pl.sched == PA_SCHED_BALANCED) {
-    if (pl.nt == 1)
-      return pl.stream ? reinterpret_cast<const void*>(mfma_attn_balanced<D, BS, 1, true>)
-                       : reinterpret_cast<const void*>(mfma_attn_balanced<D, BS, 1, false>);
-    return pl.stream ? reinterpret_cast<const void*>(mfma_attn_balanced<D, BS, 2, true>)
-                     : reinterpret_cast<const void*>(mfma_attn_balanced<D, BS, 2, false>);
-  }
-  if (pl.path == PA_PATH_MFMA) {
-    if (pl.nt == 1)
-      return pl.stream ? reinterpret_cast<const void*>(mfma_attn<D, BS, 1, true>)
-                       : reinterpret_cast<const void*>(mfma_attn<D, BS, 1, false>);
-    return pl.stream ? reinterpret_cast<const void*>(mfma_attn<D, BS, 2, true>)
-                     : reinterpret_cast<const void*>(mfma_attn<D, BS, 2, false>);
-  }
+  if (pl.path == PA_PATH_MFMA) return pl.nt == 1 ? mfma_kernel<D, BS, 1>(pl) : mfma_kernel<D, BS, 2>(pl);
   return dtype == PA_DTYPE_F32 ? reinterpret_cast<const void*>(valu_attn<float, D, BS>)
                                : reinterpret_cast<const void*>(valu_attn<uint16_t, D, BS>);
 }
@@ -1154,6 +1348,14 @@ extern "C" pa_status pa_attention(const pa_attn_desc* desc, const void* q, const
   args.counters = nullptr;
   args.part_ml = nullptr;
   args.part_o = nullptr;
+  args.k_scales = nullptr;
+  args.v_scales = nullptr;
+  if (pl.kv8) {
+    const int64_t codes = pa::fp8_codes_bytes(desc->num_blocks, desc->num_kv_heads, desc->block_size,
+                                              desc->head_dim);
+    args.k_scales = reinterpret_cast<const float*>(static_cast<const char*>(k_pool) + codes);
+    args.v_scales = reinterpret_cast<const float*>(static_cast<const char*>(v_pool) + codes);
+  }
   if (pl.sched == PA_SCHED_BALANCED) {
     char* w = static_cast<char*>(workspace);
     args.counters = reinterpret_cast<int32_t*>(w);

@@ -21,7 +21,13 @@ namespace pa {
 
 inline bool supported_block_size(int32_t bs) { return bs == 16 || bs == 32; }
 inline bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
-inline int32_t elem_bytes(int32_t dtype) { return dtype == PA_DTYPE_F32 ? 4 : 2; }
+inline int32_t elem_bytes(int32_t dtype) {
+  return dtype == PA_DTYPE_F32 ? 4 : (dtype == PA_DTYPE_BF16 ? 2 : 1);
+}
+// Bytes of the codes part of an FP8 pool buffer (the scales follow).
+inline int64_t fp8_codes_bytes(int64_t num_blocks, int64_t hkv, int64_t bs, int64_t d) {
+  return num_blocks * hkv * bs * d;
+}
 
 // Host planning of a write (allocation on growth, copy-on-write on shared
 // blocks). copies receives (src, dst) pairs; slots may be null.

@@ -29,6 +29,17 @@ extern "C" const char* pa_status_string(pa_status s) {
   }
 }
 
+extern "C" int64_t pa_pool_buffer_bytes(int32_t num_blocks, int32_t block_size,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t dtype) {
+  if (num_blocks <= 0 || num_kv_heads <= 0 || !pa::supported_block_size(block_size) ||
+      !pa::supported_head_dim(head_dim))
+    return -1;
+  const int64_t slots = int64_t(num_blocks) * num_kv_heads * block_size;
+  if (dtype == PA_DTYPE_F32 || dtype == PA_DTYPE_BF16) return slots * head_dim * pa::elem_bytes(dtype);
+  if (dtype == PA_DTYPE_FP8_E4M3) return slots * head_dim + slots * int64_t(sizeof(float));
+  return -1;
+}
+
 extern "C" int64_t pa_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads,
                                          int32_t head_dim, int32_t elem_bytes) {
   if (num_layers <= 0 || num_kv_heads <= 0 || head_dim <= 0 || elem_bytes <= 0) return -1;
@@ -43,7 +54,8 @@ extern "C" pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, int3
   *out = nullptr;
   if (num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
     return PA_ERR_INVALID_ARG;
-  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16 && dtype != PA_DTYPE_FP8_E4M3)
+    return PA_ERR_UNSUPPORTED;
   if (!pa::supported_block_size(block_size) || !pa::supported_head_dim(head_dim))
     return PA_ERR_UNSUPPORTED;
   pa_pool* p = new (std::nothrow) pa_pool();

@@ -47,13 +47,20 @@ def oracle_out(w):
 
 
 def oracle_rows(w, seqs):
-    """Oracle for selected sequences, from their contiguous (never-paged) K/V."""
+    """Oracle for selected sequences, from their contiguous (never-paged) K/V
+    (for an FP8 pool: the dequantised values of their E4M3 quantisation)."""
+    from oracle import fp8
     cfg = w.cfg
     res = {}
     for b in seqs:
         k, v = w.logical_kv(b)
+        kv_dtype = None
+        if cfg.kv_dtype == "fp8":
+            k = fp8.dequantize(*fp8.quantize_rows(to_f64(k, "bf16").astype(np.float32)))
+            v = fp8.dequantize(*fp8.quantize_rows(to_f64(v, "bf16").astype(np.float32)))
+            kv_dtype = "f64"
         res[b] = oatt.attention_contiguous(w.seqs[b].q, k, v, cfg.q_len, cfg.num_q_heads,
-                                           cfg.num_kv_heads, cfg.scale, cfg.dtype)
+                                           cfg.num_kv_heads, cfg.scale, cfg.dtype, kv_dtype)
     return res
 
 

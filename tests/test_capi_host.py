@@ -36,6 +36,15 @@ def test_status_strings():
     assert pa.pa_status_string(99) == "unknown status"
 
 
+def test_pool_buffer_bytes():
+    assert pa.pa_pool_buffer_bytes(16384, 32, 8, 128, pa.PA_DTYPE_BF16) == 2**30
+    assert pa.pa_pool_buffer_bytes(32, 16, 2, 64, pa.PA_DTYPE_F32) == 32 * 16 * 2 * 64 * 4
+    # FP8: one byte per element plus one fp32 scale per (block, head, slot)
+    assert pa.pa_pool_buffer_bytes(16384, 32, 8, 128, pa.PA_DTYPE_FP8_E4M3) == 2**29 + 16384 * 8 * 32 * 4
+    assert pa.pa_pool_buffer_bytes(16, 8, 2, 64, pa.PA_DTYPE_BF16) == -1
+    assert pa.pa_pool_buffer_bytes(16, 16, 2, 64, 9) == -1
+
+
 def test_kv_bytes_per_token_matches_closed_form():
     assert pa.pa_kv_bytes_per_token(80, 8, 128, 2) == 327680
     assert pa.pa_kv_bytes_per_token(1, 8, 128, 2) == 4096
@@ -222,6 +231,9 @@ def test_attention_plan_validation():
         (dict(dtype=pa.PA_DTYPE_F32, path=pa.PA_PATH_MFMA), 1, _lib.PA_ERR_UNSUPPORTED),
         (dict(waves_per_group=3), 1, _lib.PA_ERR_INVALID_ARG),
         (dict(waves_per_group=8), 1, _lib.PA_ERR_INVALID_ARG),
+        (dict(kv_format=2), 1, _lib.PA_ERR_INVALID_ARG),
+        (dict(kv_format=pa.PA_KV_FP8_E4M3, path=pa.PA_PATH_VALU), 1, _lib.PA_ERR_UNSUPPORTED),
+        (dict(kv_format=pa.PA_KV_FP8_E4M3, dtype=pa.PA_DTYPE_F32), 1, _lib.PA_ERR_UNSUPPORTED),
     ]
     for over, q_len, status in bad:
         with pytest.raises(pa.PAError) as e:

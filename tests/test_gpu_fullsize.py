@@ -12,7 +12,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 from tests.gpu_util import assert_close, oracle_rows, out_to_f64, run_gpu  # noqa: E402
 
 SAMPLE = {"tiny_f32": None, "llama3_8b_decode": [0, 17, 63], "llama3_70b_decode": [0, 41],
-          "prefix_verify": [0, 64, 127], "long_ctx_split": [3]}
+          "prefix_verify": [0, 64, 127], "long_ctx_split": [3], "llama3_70b_decode_fp8": [0, 63]}
 
 
 def model_tables(w):

@@ -20,6 +20,12 @@ SMALL = {
     "verify": ("prefix_verify", dict(batch=6, prefix_len=40, len_lo=20, len_hi=300)),
     "verify_aligned": ("prefix_verify", dict(batch=5, prefix_len=64, len_lo=5, len_hi=200)),
     "long": ("long_ctx_split", dict(batch=2, len_const=3000)),
+    "70b_fp8": ("llama3_70b_decode_fp8", dict(batch=3, len_const=333)),
+    "8b_fp8": ("llama3_8b_decode", dict(batch=5, len_lo=17, len_hi=700, kv_dtype="fp8")),
+    "verify_fp8": ("prefix_verify", dict(batch=6, prefix_len=40, len_lo=20, len_hi=300, kv_dtype="fp8")),
+    "long_fp8": ("long_ctx_split", dict(batch=2, len_const=3000, kv_dtype="fp8")),
+    "d64_fp8": ("llama3_70b_decode_fp8", dict(batch=3, len_const=0, lens=(1, 64, 77), head_dim=64,
+                                              num_q_heads=16, num_kv_heads=4)),
 }
 _cache = {}
 
@@ -38,6 +44,8 @@ CASES = [
     ("70b", MFMA, 0), ("70b", VALU, 0), ("70b", MFMA, 64),
     ("verify", MFMA, 0), ("verify", MFMA, 64), ("verify_aligned", MFMA, 0),
     ("long", MFMA, 512), ("long", VALU, 512), ("long", MFMA, 0),
+    ("70b_fp8", MFMA, 0), ("70b_fp8", MFMA, 64), ("8b_fp8", MFMA, 0), ("8b_fp8", MFMA, 128),
+    ("verify_fp8", MFMA, 0), ("long_fp8", MFMA, 512), ("long_fp8", MFMA, 0), ("d64_fp8", MFMA, 0),
 ]
 
 
@@ -133,9 +141,10 @@ def test_balanced_repeat_calls_reuse_workspace(key):
             assert np.array_equal(out_bits(o), first)
 
 
-@pytest.mark.parametrize("key", ["8b", "verify", "tiny_f32"])
+@pytest.mark.parametrize("key", ["8b", "verify", "tiny_f32", "verify_fp8", "d64_fp8"])
 def test_pool_bytes_and_tables_match_model(key):
-    """pa_write_kv (allocation, copy-on-write, scatter) gives the model's pool bit for bit."""
+    """pa_write_kv (allocation, copy-on-write, scatter, FP8 quantisation) gives
+    the model's pool bit for bit."""
     w, _ = small(key)
     from paged_kv_cache_218_amd.cache import PagedKVCache
     import paged_kv_cache_218_amd as pa
@@ -145,6 +154,14 @@ def test_pool_bytes_and_tables_match_model(key):
     assert np.array_equal(cache.tables, tables) and cache.live == live
     assert [pa.pa_block_refcount(cache.pool, b) for b in range(w.num_blocks)] == model.refcount
     assert list(pa.pa_pool_free_list(cache.pool)) == model.free_list()
+    if w.cfg.kv_dtype == "fp8":
+        codes = pool.k.size
+        kb, vb = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
+        assert np.array_equal(kb[:codes], pool.k.reshape(-1))
+        assert np.array_equal(vb[:codes], pool.v.reshape(-1))
+        assert np.array_equal(kb[codes:].view(np.uint32), pool.k_scale.reshape(-1).view(np.uint32))
+        assert np.array_equal(vb[codes:].view(np.uint32), pool.v_scale.reshape(-1).view(np.uint32))
+        return
     iview = torch.int32 if w.cfg.dtype == "f32" else torch.int16
     nview = np.int32 if w.cfg.dtype == "f32" else np.int16
     assert np.array_equal(cache.k_pool.cpu().view(iview).numpy(), pool.k.view(nview))
