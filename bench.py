@@ -9,8 +9,9 @@ Llama-3-70B-shaped layer, 64 sequences x 8192 tokens, bf16, block size 32.
 Prints one JSON line on stdout; progress goes to stderr.
 
 Algorithmic bytes of a step: every sequence's K and V once
-(sum_b L_b * 2 * H_kv * d * elem), q in and out once (2 * B * q_len * H_q * d
-* elem), the block-table entries read (sum_b ceil(L_b/bs) * 4) and the
+(sum_b L_b * 2 * H_kv * d * elem; for an FP8 cache d + 4 bytes per token, head
+and K/V: the codes and the fp32 scale), q in and out once (2 * B * q_len *
+H_q * d * elem), the block-table entries read (sum_b ceil(L_b/bs) * 4) and the
 context lengths (4 * B).
 """
 from __future__ import annotations
@@ -38,7 +39,10 @@ def log(*a):
 
 def algorithmic_bytes(cfg, lens) -> int:
     esz = cfg.elem_bytes
-    kv = int(lens.astype(np.int64).sum()) * 2 * cfg.num_kv_heads * cfg.head_dim * esz
+    if cfg.kv_dtype == "fp8":   # one byte per element plus one fp32 scale per token, head, K and V
+        kv = int(lens.astype(np.int64).sum()) * 2 * cfg.num_kv_heads * (cfg.head_dim + 4)
+    else:
+        kv = int(lens.astype(np.int64).sum()) * 2 * cfg.num_kv_heads * cfg.head_dim * esz
     qo = 2 * cfg.batch * cfg.q_len * cfg.num_q_heads * cfg.head_dim * esz
     tables = int((-(-lens.astype(np.int64) // cfg.block_size)).sum()) * 4 + 4 * cfg.batch
     return kv + qo + tables
@@ -89,7 +93,8 @@ def kernel_name(cfg, plan, desc) -> str:
     base = "mfma_attn_balanced" if plan.schedule == 1 else "mfma_attn"
     nt = 2 if cfg.group * cfg.q_len > 16 else 1
     stream = "false" if desc.kv_shared else "true"
-    return f"{base}<{cfg.head_dim}, {cfg.block_size}, {nt}, {stream}>"
+    kv8 = "true" if desc.kv_format else "false"
+    return f"{base}<{cfg.head_dim}, {cfg.block_size}, {nt}, {stream}, {kv8}>"
 
 
 def source_digest() -> str:
@@ -137,7 +142,8 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_bytes: int =
     max_blocks = int(-(-int(lens.max()) // cfg.block_size))
     desc = pa.make_desc(cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size,
                         max_blocks, nb, pa.PA_DTYPE_F32 if cfg.dtype == "f32" else pa.PA_DTYPE_BF16,
-                        int(lens.max()), 0, max(cfg.partition_tokens, 0), 0, int(cfg.prefix_len > 0))
+                        int(lens.max()), 0, max(cfg.partition_tokens, 0), 0, int(cfg.prefix_len > 0),
+                        pa.PA_KV_FP8_E4M3 if cfg.kv_dtype == "fp8" else pa.PA_KV_SAME)
     plan = pa.pa_attention_plan(desc, cfg.q_len)
     kernel = kernel_name(cfg, plan, desc)
     out = {"workload": workload, "kernel": kernel, "source_sha256": source_digest(),
@@ -283,6 +289,7 @@ def main():
             "context_tokens": {"min": int(w.lens.min()), "max": max_ctx, "mean": float(w.lens.mean())},
             "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
             "block_size": cfg.block_size, "num_blocks": w.num_blocks, "prefix_len": cfg.prefix_len,
+            "kv_storage": "fp8_e4m3+scales" if cfg.kv_dtype == "fp8" else cfg.dtype,
             "path": path_name, "partition_tokens": plan.partition_tokens,
             "schedule": {0: "partitions", 1: "balanced"}[plan.schedule], "kv_shared": int(desc.kv_shared),
             "partitions": plan.num_partitions, "waves_per_group": plan.waves_per_group,
