@@ -12,10 +12,13 @@ Contents (each function cites the passage of the pages it follows):
   attention  softmax(q K^T * scale) V over the gathered context (fp64)
   split      partition-local attention and the log-sum-exp merge (fp64)
   kvbytes    closed form for KV-cache bytes per token
+  fp8        OCP E4M3 codec and the per-(token, KV head) quantiser
+  tree       tree-structured verification: ancestor masks, visible positions
 
 Pins (tests marked ``not gpu``): brute-force scalar loops, torch's fp64
 scaled_dot_product_attention on the never-paged K/V, the literal block tables
 printed on the pages, the closed form's printed values, invariants (placement,
-prefix sharing, one-token context, zero query, causal rows) and planted
-mistakes that the pins must catch. No function here is "parity unpinned".
+prefix sharing, one-token context, zero query, causal rows), torch's
+float8_e4m3fn for the codec, parent-pointer walks for the tree masks, and
+planted mistakes that the pins must catch. No function here is "parity unpinned".
 """

@@ -2,7 +2,8 @@
 catch each one: a wrong GQA head map, a wrong scale, an off-by-one causal
 bound, K and V swapped, a transposed V slot, a wrong in-block offset, a
 missing softmax normalisation, a merge without the max rescale, a doubled
-byte count, and a FIFO free list."""
+byte count, a FIFO free list, two FP8 codec mistakes, and two tree-mask
+mistakes (ancestor sets cut to the parent, draft positions shifted by one)."""
 import numpy as np
 import pytest
 
@@ -16,6 +17,8 @@ from tests import test_oracle_pins as pins
 from tests import test_allocator_model as apins
 from tests import test_oracle_fp8 as fpins
 import oracle.fp8 as ofp8
+import oracle.tree as otree
+from tests import test_oracle_tree as tpins
 
 
 def run_pins():
@@ -36,6 +39,8 @@ def run_pins():
         "fp8_attention": lambda: fpins.test_fp8_pool_attention_vs_torch_sdpa(
             "llama3_70b_decode_fp8", dict(batch=2, len_const=100)),
         "cow": apins.test_four_samples_share_prompt_then_copy_only_the_diverging_block,
+        "tree_literal": tpins.test_ancestor_masks_literal,
+        "tree_sdpa": lambda: tpins.test_tree_vs_torch_sdpa_with_parent_walk_mask(dict()),
     }
     failed = []
     for name, fn in checks.items():
@@ -91,6 +96,19 @@ def _merge_no_rescale(m, l, o):
     return (w[:, :, None] * o).sum(axis=0) / w.sum(axis=0)[:, None]
 
 
+def _ancestors_parent_only(parents):
+    return [(1 << i) | ((1 << int(p)) if p >= 0 else 0) for i, p in enumerate(parents)]
+
+
+_real_visible = otree.visible_positions
+
+
+def _visible_shifted(L, q_len, mask, i):
+    pos = _real_visible(L, q_len, mask, i)
+    ctx = L - q_len
+    return np.where(pos >= ctx, pos - 1, pos)
+
+
 class FifoPool(oalloc.BlockPoolModel):
     def alloc(self):
         if not self._stack:
@@ -122,6 +140,8 @@ MUTANTS = {
     "fp8_exponent_bias_8": lambda mp: mp.setattr(ofp8, "_TABLE", ofp8.e4m3_decode_table() / 2.0),
     "fp8_scale_not_applied": lambda mp: mp.setattr(ofp8, "dequantize",
                                                    lambda c, s: ofp8.e4m3_decode(c) * 1.0),
+    "tree_ancestors_parent_only": lambda mp: mp.setattr(otree, "ancestor_masks", _ancestors_parent_only),
+    "tree_nodes_shifted": lambda mp: mp.setattr(otree, "visible_positions", _visible_shifted),
 }
 
 

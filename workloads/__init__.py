@@ -17,4 +17,5 @@ from .gen import (  # noqa: F401
     generate,
     pool_blocks,
     sequence,
+    tree_parents,
 )

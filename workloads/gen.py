@@ -27,6 +27,7 @@ SEED = 218
 _LEN_STREAM = 1_000_000
 _PERM_STREAM = 1_000_001
 _PREFIX_STREAM = 1_000_002
+_TREE_STREAM = 1_000_003
 
 
 @dataclass(frozen=True)
@@ -58,6 +59,10 @@ class Config:
     # fraction of key vectors per (sequence, kv head) scaled by key_outlier_scale
     key_outlier_frac: float = 0.0
     key_outlier_scale: float = 1.0
+    # shape of the q_len drafted tokens: "" = a chain (each continues the one
+    # before), "random" = a random tree per sequence, "shared" = one random
+    # tree for the whole batch. A tree is given by parent indices only.
+    tree: str = ""
 
     @property
     def group(self) -> int:
@@ -91,6 +96,12 @@ CONFIGS = {
                num_kv_heads=8, head_dim=128, block_size=32, dtype="bf16",
                len_const=131072, partition_tokens=512,
                key_outlier_frac=0.01, key_outlier_scale=8.0),
+        # speculative verification of a tree of 8 drafted tokens per sequence
+        # (4 query heads per KV head x 8 nodes = 32 rows per KV head)
+        Config("tree_verify", 5, batch=128, q_len=8, num_q_heads=32,
+               num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
+               prefix_len=512, len_lo=512, len_hi=3584, pool_slack=1.25,
+               tree="random"),
         # the 70B-shaped layer with an FP8 KV cache (same seeds and values as
         # llama3_70b_decode; the pool holds their E4M3 quantisation)
         Config("llama3_70b_decode_fp8", 2, batch=64, q_len=1, num_q_heads=64,
@@ -159,6 +170,22 @@ def _values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
     return x if dtype == "f32" else bf16_bits_from_f32(x)
 
 
+def tree_parents(cfg: Config) -> Optional[np.ndarray]:
+    """int32 [B][q_len] parent index of each drafted token (-1: continues the
+    context), parents before children; None for a plain chain. Node j's parent
+    is uniform over {-1, 0, ..., j-1}."""
+    if not cfg.tree:
+        return None
+    if cfg.tree not in ("random", "shared"):
+        raise ValueError(f"unknown tree shape {cfg.tree!r}")
+    n_trees = 1 if cfg.tree == "shared" else cfg.batch
+    out = np.empty((n_trees, cfg.q_len), dtype=np.int32)
+    for t in range(n_trees):
+        rng = _rng(cfg.cfg_id, _TREE_STREAM, t)
+        out[t] = [rng.integers(-1, j) for j in range(cfg.q_len)]
+    return np.repeat(out, cfg.batch, axis=0) if n_trees == 1 else out
+
+
 @dataclass
 class SeqData:
     """One sequence's query rows and its private (non-prefix) keys and values.
@@ -196,6 +223,7 @@ class Workload:
     seqs: List[SeqData] = field(default_factory=list)
     prefix_k: Optional[np.ndarray] = None   # [prefix_len][H_kv][d]
     prefix_v: Optional[np.ndarray] = None
+    tree_parents: Optional[np.ndarray] = None   # int32 [B][q_len], or None (chain)
 
     @property
     def max_blocks(self) -> int:
@@ -216,7 +244,7 @@ class Workload:
 def generate(cfg: Config, threads: int = 8) -> Workload:
     lens = context_lengths(cfg)
     nb = pool_blocks(cfg, lens)
-    w = Workload(cfg, lens, nb, free_order(cfg, nb))
+    w = Workload(cfg, lens, nb, free_order(cfg, nb), tree_parents=tree_parents(cfg))
     if cfg.prefix_len:
         rng = _rng(cfg.cfg_id, _PREFIX_STREAM)
         shape = (cfg.prefix_len, cfg.num_kv_heads, cfg.head_dim)
