@@ -3,8 +3,9 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--path auto|mfma|valu]
                     [--partition-tokens N] [--no-cpu-baseline] [--copy-probe]
 
-A step is one pa_attention call over the whole batch of the workload (every
-sequence, every query head), inputs resident in HBM. Default workload: the
+A step is one pa_attention call (pa_attention_tree for a tree of drafted
+tokens) over the whole batch of the workload (every sequence, every query
+head), inputs resident in HBM. Default workload: the
 Llama-3-70B-shaped layer, 64 sequences x 8192 tokens, bf16, block size 32.
 Prints one JSON line on stdout; progress goes to stderr.
 
@@ -52,6 +53,7 @@ def cpu_baseline(w, budget_s: float = 15.0):
     """The fp64 oracle (gather through the block table, then the definition)
     on as many whole sequences as fit in about budget_s seconds."""
     from oracle import attention as oatt
+    from oracle import tree as otree
     from oracle.build import build_pool
     try:
         from threadpoolctl import threadpool_info
@@ -64,8 +66,12 @@ def cpu_baseline(w, budget_s: float = 15.0):
     done, t_used = 0, 0.0
     for b in range(cfg.batch):
         t0 = time.perf_counter()
-        oatt.attention_paged_seq(w.seqs[b].q, pool, tables[b], int(w.lens[b]), cfg.q_len,
-                                 cfg.num_q_heads, cfg.scale)
+        if w.tree_parents is None:
+            oatt.attention_paged_seq(w.seqs[b].q, pool, tables[b], int(w.lens[b]), cfg.q_len,
+                                     cfg.num_q_heads, cfg.scale)
+        else:
+            otree.attention_tree_seq(w.seqs[b].q, pool, tables[b], int(w.lens[b]), cfg.q_len,
+                                     otree.ancestor_masks(w.tree_parents[b]), cfg.num_q_heads, cfg.scale)
         t_used += time.perf_counter() - t0
         done += 1
         if t_used >= budget_s:
@@ -94,7 +100,8 @@ def kernel_name(cfg, plan, desc) -> str:
     nt = 2 if cfg.group * cfg.q_len > 16 else 1
     stream = "false" if desc.kv_shared else "true"
     kv8 = "true" if desc.kv_format else "false"
-    return f"{base}<{cfg.head_dim}, {cfg.block_size}, {nt}, {stream}, {kv8}>"
+    tree = "true" if cfg.tree else "false"
+    return f"{base}<{cfg.head_dim}, {cfg.block_size}, {nt}, {stream}, {kv8}, {tree}>"
 
 
 def source_digest() -> str:
@@ -239,13 +246,22 @@ def main():
     desc = cache.desc(cfg.num_q_heads, max_ctx, path, pt, args.waves)
     plan = pa.pa_attention_plan(desc, cfg.q_len)
     out = torch.empty_like(q)
-    ws = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device="cuda")
+    # zero-filled: the balanced schedule's arrival counters start at zero
+    ws = torch.zeros(max(plan.workspace_bytes, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    masks = None
+    if w.tree_parents is not None:   # tree verification: ancestor masks from the library's helper
+        from paged_kv_cache_218_amd.cache import tree_masks_to_device
+        masks = tree_masks_to_device(w.tree_parents)
     torch.cuda.synchronize()
 
     def step():
-        pa.pa_attention(desc, q, cache.k_pool, cache.v_pool, tables_d, lens_d, cfg.q_len, cfg.scale,
-                        out, ws if plan.workspace_bytes else None, stream)
+        if masks is None:
+            pa.pa_attention(desc, q, cache.k_pool, cache.v_pool, tables_d, lens_d, cfg.q_len, cfg.scale,
+                            out, ws if plan.workspace_bytes else None, stream)
+        else:
+            pa.pa_attention_tree(desc, q, cache.k_pool, cache.v_pool, tables_d, lens_d, cfg.q_len, masks,
+                                 cfg.q_len, cfg.scale, out, ws if plan.workspace_bytes else None, stream)
 
     for _ in range(args.warmup):
         step()
@@ -290,6 +306,7 @@ def main():
             "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
             "block_size": cfg.block_size, "num_blocks": w.num_blocks, "prefix_len": cfg.prefix_len,
             "kv_storage": "fp8_e4m3+scales" if cfg.kv_dtype == "fp8" else cfg.dtype,
+            "drafted_tokens": f"tree ({cfg.tree})" if cfg.tree else ("chain" if cfg.q_len > 1 else "none"),
             "path": path_name, "partition_tokens": plan.partition_tokens,
             "schedule": {0: "partitions", 1: "balanced"}[plan.schedule], "kv_shared": int(desc.kv_shared),
             "partitions": plan.num_partitions, "waves_per_group": plan.waves_per_group,

@@ -93,6 +93,10 @@ enum { PA_PATH_AUTO = 0, PA_PATH_VALU = 1, PA_PATH_MFMA = 2 };
  *   that finishes its last share (one kernel, no second launch). */
 enum { PA_SCHED_PARTITIONS = 0, PA_SCHED_BALANCED = 1 };
 
+/* Largest tree of drafted tokens pa_attention_tree takes: one 32-bit
+ * visibility mask per node. */
+enum { PA_TREE_MAX_NODES = 32 };
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* pa_status_string(pa_status s);
 
@@ -281,6 +285,44 @@ pa_status pa_attention(const pa_attn_desc* desc, const void* q, const void* k_po
                        const void* v_pool, const int32_t* block_tables,
                        const int32_t* context_lens, int32_t q_len, float scale, void* out,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tree-structured verification ("Mở rộng Quy mô và Triển khai", section
+ * "Giải mã Suy đoán", its variants: parallel decoding drafts a tree of
+ * candidate continuations and the target verifies the whole tree in one
+ * pass). The q_len drafted tokens are the nodes of a tree, node j at position
+ * L_b-q_len+j (its K/V written there); node i sees the context (positions
+ * 0..L_b-q_len-1) and the nodes whose bit is set in its mask:
+ *   tree_mask    device uint32 [B][mask_stride] (mask_stride > 0) or [q_len]
+ *                shared by every sequence (mask_stride == 0); bit j of
+ *                tree_mask[b*mask_stride + i] lets row i of sequence b see
+ *                node j. Bit i is taken as set (a node always sees itself);
+ *                bits at or above q_len are ignored. pa_tree_masks turns
+ *                parent indices into ancestor masks.
+ *   mask_stride  0, or >= q_len
+ * Everything else is pa_attention's, which this equals when every mask is
+ * the causal one (bits 0..i). PA_ERR_INVALID_ARG for a null tree_mask,
+ * q_len > PA_TREE_MAX_NODES or a bad stride, besides pa_attention's checks.
+ * Mask contents are not validated: any 32-bit value is a valid mask. */
+pa_status pa_attention_tree(const pa_attn_desc* desc, const void* q, const void* k_pool,
+                            const void* v_pool, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t q_len,
+                            const uint32_t* tree_mask, int32_t mask_stride, float scale,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The hipError_t of this thread's last HIP call that made a pa_* function
+ * return PA_ERR_HIP (0 if none yet), and the HIP runtime's name for a
+ * hipError_t value. Diagnostics only. */
+int32_t pa_last_hip_error(void);
+const char* pa_hip_error_name(int32_t hip_error);
+
+/* Host helper: ancestor masks of a tree given by parent indices.
+ *   parents  host int32 [n]; parents[i] is -1 (node i continues the context)
+ *            or an earlier node (0 <= parents[i] < i)
+ *   masks    host uint32 [n] out; bit j of masks[i] is set iff node j is node
+ *            i or one of its ancestors
+ * PA_ERR_INVALID_ARG for null pointers, n outside [1, PA_TREE_MAX_NODES] or a
+ * parent that is not an earlier node (masks then unspecified). */
+pa_status pa_tree_masks(const int32_t* parents, int32_t n, uint32_t* masks);
 
 #ifdef __cplusplus
 }

@@ -67,6 +67,22 @@ def attention_tree_seq(q, pool: HostPool, table, ctx_len: int, q_len: int, masks
     return out
 
 
+def attention_tree_contiguous(q, k, v, q_len: int, num_q_heads: int, num_kv_heads: int, masks,
+                              scale: float, dtype: str, kv_dtype: str = None) -> np.ndarray:
+    """One sequence with contiguous (never-paged) K/V [L][H_kv][d]; masks [q_len]."""
+    G = num_q_heads // num_kv_heads
+    L = k.shape[0]
+    qf = to_f64(q, dtype)
+    out = np.empty(qf.shape, dtype=np.float64)
+    for g in range(num_kv_heads):
+        kf = to_f64(k[:, g, :], kv_dtype or dtype)
+        vf = to_f64(v[:, g, :], kv_dtype or dtype)
+        for i in range(q_len):
+            pos = visible_positions(L, q_len, masks[i], i)
+            out[i, g * G:(g + 1) * G, :] = attend(qf[i, g * G:(g + 1) * G, :], kf[pos], vf[pos], scale)
+    return out
+
+
 def attention_tree(q, pool: HostPool, tables, ctx_lens, q_len: int, masks, scale: float,
                    q_dtype: str = None) -> np.ndarray:
     """Batch form. q [B][q_len][H_q][d]; masks [B][q_len]. float64 out."""

@@ -15,6 +15,7 @@ PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3 = 0, 1, 2
 PA_KV_SAME, PA_KV_FP8_E4M3 = 0, 1
 PA_PATH_AUTO, PA_PATH_VALU, PA_PATH_MFMA = 0, 1, 2
 PA_SCHED_PARTITIONS, PA_SCHED_BALANCED = 0, 1
+PA_TREE_MAX_NODES = 32
 
 i32, i64, vp, f32, sz = C.c_int32, C.c_int64, C.c_void_p, C.c_float, C.c_size_t
 pi32 = C.POINTER(C.c_int32)
@@ -53,10 +54,22 @@ SIGNATURES = [
     ("pa_attention_plan", i32, [C.POINTER(AttnDesc), i32, C.POINTER(AttnPlan)]),
     ("pa_attention_workspace_size", sz, [C.POINTER(AttnDesc), i32]),
     ("pa_attention", i32, [C.POINTER(AttnDesc), vp, vp, vp, vp, vp, i32, f32, vp, vp, sz, vp]),
+    ("pa_attention_tree", i32, [C.POINTER(AttnDesc), vp, vp, vp, vp, vp, i32, vp, i32, f32, vp, vp, sz, vp]),
+    ("pa_tree_masks", i32, [pi32, i32, C.POINTER(C.c_uint32)]),
+    ("pa_last_hip_error", i32, []),
+    ("pa_hip_error_name", C.c_char_p, [i32]),
 ]
 
 
 def _load() -> C.CDLL:
+    # torch ships its own HIP runtime under the same soname as ROCm's. Loading
+    # torch first makes this library bind to that one runtime; loaded the other
+    # way round the process holds two HIP runtimes, and device pointers and
+    # streams from torch mean nothing to the library's (hipErrorNoDevice).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_218_amd.build` "
                           "(hipcc, gfx950); there is no fallback implementation")

@@ -19,6 +19,9 @@ from ._lib import AttnDesc, AttnPlan, lib
 class PAError(RuntimeError):
     def __init__(self, status: int, where: str):
         msg = lib.pa_status_string(status).decode()
+        if status == _lib.PA_ERR_HIP:
+            e = lib.pa_last_hip_error()
+            msg += f" [{lib.pa_hip_error_name(e).decode()} ({e})]"
         super().__init__(f"{where}: {msg} (status {status})")
         self.status = status
 
@@ -184,3 +187,22 @@ def pa_attention(desc: AttnDesc, q, k_pool, v_pool, block_tables, context_lens, 
     _check(lib.pa_attention(C.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
                             _ptr(context_lens), q_len, scale, _ptr(out), _ptr(workspace), ws_bytes,
                             _stream(stream)), "pa_attention")
+
+
+def pa_attention_tree(desc: AttnDesc, q, k_pool, v_pool, block_tables, context_lens, q_len: int,
+                      tree_mask, mask_stride: int, scale: float, out, workspace=None, stream=None) -> None:
+    """tree_mask: device uint32 masks, [B][mask_stride] or [q_len] when mask_stride is 0
+    (a torch int32/uint32 tensor; only its bits matter)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pa_attention_tree(C.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                 _ptr(context_lens), q_len, _ptr(tree_mask), mask_stride, scale, _ptr(out),
+                                 _ptr(workspace), ws_bytes, _stream(stream)), "pa_attention_tree")
+
+
+def pa_tree_masks(parents: np.ndarray) -> np.ndarray:
+    """Ancestor masks (uint32 [n]) of a tree given by parent indices (int32 [n])."""
+    parents = np.ascontiguousarray(parents, dtype=np.int32)
+    masks = np.zeros(parents.size, dtype=np.uint32)
+    _check(lib.pa_tree_masks(_i32p(parents), parents.size, masks.ctypes.data_as(C.POINTER(C.c_uint32))),
+           "pa_tree_masks")
+    return masks

@@ -94,7 +94,9 @@ class PagedKVCache:
 
     def attention(self, q, tables_dev, lens_dev, q_len: int, scale: float, max_context: int,
                   path=_lib.PA_PATH_AUTO, partition_tokens=0, waves_per_group=0, out=None, workspace=None,
-                  stream=None):
+                  stream=None, tree_mask=None, mask_stride=None):
+        """pa_attention, or pa_attention_tree when tree_mask (device uint32/int32
+        masks, [B][q_len] by default) is given."""
         import torch
         desc = self.desc(q.shape[2], max_context, path, partition_tokens, waves_per_group)
         if out is None:
@@ -102,8 +104,13 @@ class PagedKVCache:
         need = api.pa_attention_workspace_size(desc, q_len)
         if workspace is None and need:
             workspace = self.workspace(need, q.device)
-        api.pa_attention(desc, q, self.k_pool, self.v_pool, tables_dev, lens_dev, q_len, scale, out,
-                         workspace, stream)
+        if tree_mask is None:
+            api.pa_attention(desc, q, self.k_pool, self.v_pool, tables_dev, lens_dev, q_len, scale, out,
+                             workspace, stream)
+        else:
+            stride = q_len if mask_stride is None else mask_stride
+            api.pa_attention_tree(desc, q, self.k_pool, self.v_pool, tables_dev, lens_dev, q_len, tree_mask,
+                                  stride, scale, out, workspace, stream)
         return out
 
     def workspace(self, nbytes: int, device):
@@ -153,3 +160,12 @@ def queries_to_device(w, device="cuda"):
 def lens_to_device(w, device="cuda"):
     import torch
     return torch.from_numpy(np.ascontiguousarray(w.lens, dtype=np.int32)).to(device)
+
+
+def tree_masks_to_device(parents, device="cuda"):
+    """Parent indices [B][q_len] -> device int32 [B][q_len] ancestor masks
+    (library helper pa_tree_masks, one tree per row)."""
+    import torch
+    parents = np.asarray(parents, dtype=np.int32)
+    masks = np.stack([api.pa_tree_masks(p) for p in parents]).view(np.int32)
+    return torch.from_numpy(np.ascontiguousarray(masks)).to(device)

@@ -39,6 +39,22 @@
 
 #include "pa_internal.h"
 
+namespace pa {
+namespace {
+thread_local int g_last_hip_error = 0;
+}
+pa_status hip_failed(int hip_error) {
+  g_last_hip_error = hip_error;
+  return PA_ERR_HIP;
+}
+}  // namespace pa
+
+extern "C" int32_t pa_last_hip_error(void) { return pa::g_last_hip_error; }
+
+extern "C" const char* pa_hip_error_name(int32_t hip_error) {
+  return hipGetErrorName(static_cast<hipError_t>(hip_error));
+}
+
 namespace {
 
 constexpr int kCUs = 256;              // MI355X compute units
@@ -66,6 +82,8 @@ struct AttnArgs {
   int32_t* counters;  // balanced: arrival count per segment, zero between calls
   const float* k_scales;  // FP8 pools: per (block, head, slot) scales after the codes
   const float* v_scales;
+  const uint32_t* tree_mask;  // tree verification: visibility bits per drafted row, or null (causal)
+  int32_t mask_stride;        // masks between consecutive sequences (0: one set for all)
   int32_t num_seqs, hq, hkv, group, mb, nb, q_len, max_ctx, parts, part_tokens;
   float scale_log2;  // scale * log2(e)
 };
@@ -124,6 +142,18 @@ __device__ __forceinline__ Tile decode_tile(const AttnArgs& a) {
   t.t0 = t.part * a.part_tokens;
   t.t1 = t.bad ? 0 : min(t.t0 + a.part_tokens, t.L);
   return t;
+}
+
+// Which drafted positions row i (0 <= i < q_len) of sequence b sees: bit j
+// stands for position L - q_len + j. Plain verification is causal (bits
+// 0..i); a tree of drafted tokens passes one mask per row, whose own bit is
+// always taken as set (speculative decoding variants: parallel decoding
+// verifies a whole tree of candidates in one pass; "Mở rộng Quy mô và Triển
+// khai", "Giải mã Suy đoán"). Every position before L - q_len is context,
+// visible to every row.
+__device__ __forceinline__ uint32_t row_mask(const AttnArgs& a, int b, int i) {
+  if (a.tree_mask) return a.tree_mask[int64_t(b) * a.mask_stride + i] | (1u << i);
+  return (2u << i) - 1u;  // i = 31 wraps to all ones
 }
 
 // Row r of a (b, g) group: draft position i = r / G, query head g*G + r % G.
@@ -267,7 +297,7 @@ __device__ __forceinline__ void wave_state_init(WaveState<D, NT>& st) {
 // One wavefront's share of a piece: steps first, first+W, ... < end of
 // sequence b (context L), KV head g. Every step covers 32 tokens; tokens at
 // or past L, and tokens after a row's causal limit, are masked.
-template <int D, int BS, int NT, bool STREAM, bool KV8>
+template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE>
 __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int first, int end, int W,
                                 WaveState<D, NT>& st) {
   constexpr int KS = D / 32;  // k-steps over the head dim for QK
@@ -287,11 +317,17 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
   // d = 64(ks/2) + 16j + 8(ks%2) .. +7 (FP8 pools, where one 16-byte load
   // holds two k-steps of a token's 64-element slab)
   u32x4 qop[NT][KS];
-  int lim[NT];  // last visible position of this lane's row
+  // causal rows: last visible position; tree rows: the drafted positions seen
+  int lim[NT];
+  uint32_t vbits[NT];
+  const int ctx_end = L - a.q_len;  // first drafted position
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = nt * 16 + n;
-    lim[nt] = L - a.q_len + min(r, R - 1) / a.group;
+    const int row_i = min(r, R - 1) / a.group;
+    if constexpr (TREE)
+      vbits[nt] = row_mask(a, b, row_i) & (a.q_len >= 32 ? ~0u : (1u << a.q_len) - 1u);
+    else lim[nt] = ctx_end + row_i;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = {0, 0, 0, 0};
@@ -303,6 +339,23 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
       qop[nt][ks] = v;
     }
   }
+
+  // Tree rows: visibility of the lane's 8 tokens tb + 8j .. +7 as bits 0..7,
+  // read from a 64-bit word whose low half stands for the 32 positions
+  // before the drafted ones (context) and whose high half is the row's mask
+  // (bits at or past q_len cleared, so positions at or past L are hidden).
+  auto tree_bits = [&](int tb, int nt) -> uint32_t {
+    const int off0 = tb + 8 * j - ctx_end;  // drafted index of the lane's first token
+    if (off0 < -32) return 0xFFu;
+    if (off0 >= 32) return 0u;
+    const uint64_t w = (uint64_t(vbits[nt]) << 32) | 0xFFFFFFFFull;
+    return uint32_t(w >> (off0 + 32)) & 0xFFu;
+  };
+  // token tok (= tb + 8j + e) is visible to this lane's row of tile nt
+  auto visible = [&](int tok, int nt, uint32_t tbits, int e) -> bool {
+    if constexpr (TREE) return (tbits >> e) & 1u;
+    else return tok < L && tok <= lim[nt];
+  };
 
   if constexpr (KV8) {
     const uint8_t* __restrict__ kc = static_cast<const uint8_t*>(a.k_pool);
@@ -398,12 +451,13 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
         float s2[8];
         bool vis[8];
         float mx = -INFINITY;
+        const uint32_t tbits = TREE ? tree_bits(tb, nt) : 0u;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int e = 4 * i + r, tok = tb + 8 * j + e;
-            vis[e] = tok < L && tok <= lim[nt];
+            const int e = 4 * i + r;
+            vis[e] = visible(tb + 8 * j + e, nt, tbits, e);
             const float v = vis[e] ? sc[i][r] * buf.ks[i][r] * a.scale_log2 : -INFINITY;
             s2[e] = v;
             mx = fmaxf(mx, v);
@@ -528,12 +582,12 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
         // mask and scale; e = 4*i + r is token tb + 8j + e
         float s2[8];
         float mx = -INFINITY;
+        const uint32_t tbits = TREE ? tree_bits(tb, nt) : 0u;
   #pragma unroll
         for (int i = 0; i < 2; ++i)
   #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int tok = tb + 8 * j + 4 * i + r;
-            const bool vis = tok < L && tok <= lim[nt];
+            const bool vis = visible(tb + 8 * j + 4 * i + r, nt, tbits, 4 * i + r);
             const float v = vis ? sc[i][r] * a.scale_log2 : -INFINITY;
             s2[4 * i + r] = v;
             mx = fmaxf(mx, v);
@@ -632,7 +686,7 @@ __device__ __forceinline__ void combine_waves(const float* smem, int W, int R, i
 
 // Fixed partitions: workgroup = (sequence, KV head, partition); partitions
 // that do not cover the whole sequence leave partials for lse_merge.
-template <int D, int BS, int NT, bool STREAM, bool KV8>
+template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE>
 __global__ __launch_bounds__(256, 2) void mfma_attn(AttnArgs a) {
   extern __shared__ float smem[];
   const int W = blockDim.x / 64, wave = threadIdx.x / 64;
@@ -643,7 +697,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn(AttnArgs a) {
   WaveState<D, NT> st;
   wave_state_init(st);
   const int s0 = t.t0 / kStep, s1 = (t.t1 + kStep - 1) / kStep;
-  mfma_wave_steps<D, BS, NT, STREAM, KV8>(a, t.b, t.g, t.L, s0 + wave, s1, W, st);
+  mfma_wave_steps<D, BS, NT, STREAM, KV8, TREE>(a, t.b, t.g, t.L, s0 + wave, s1, W, st);
   const bool bad = park_states(st, R, smem);
   merge_and_store<uint16_t, D>(a, t, R, R, W, smem, smem + W * R, smem + 2 * W * R, bad);
 }
@@ -666,7 +720,7 @@ __device__ __forceinline__ int64_t owner(int64_t x, int64_t S, int64_t N) {
   return k;
 }
 
-template <int D, int BS, int NT, bool STREAM, bool KV8>
+template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE>
 __global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
   extern __shared__ float smem[];  // [B+1] step prefix sums, then the parked states
   const int W = blockDim.x / 64, wave = threadIdx.x / 64;
@@ -741,7 +795,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
     const int L = a.lens[b];
     WaveState<D, NT> st;
     wave_state_init(st);
-    mfma_wave_steps<D, BS, NT, STREAM, KV8>(a, b, g, L, first + wave, last, W, st);
+    mfma_wave_steps<D, BS, NT, STREAM, KV8, TREE>(a, b, g, L, first + wave, last, W, st);
     const bool bad = park_states(st, R, park);
     const int64_t seg = int64_t(b) * a.hkv + g;
     const bool whole = first == 0 && last == nb;
@@ -897,6 +951,10 @@ __global__ __launch_bounds__(256) void valu_attn(AttnArgs a) {
     for (int k = 0; k < DPL; ++k) acc[r][k] = 0.f;
   }
   bool poisoned = false;
+  uint32_t vbits[RM];  // drafted positions each row sees
+#pragma unroll
+  for (int r = 0; r < RM; ++r) vbits[r] = row_mask(a, t.b, min(r, R - 1) / a.group);
+  const int ctx_end = t.L - a.q_len;
   float* pw = p_s + wave * RM * 64;                              // f32 probabilities
   uint16_t* pwh = reinterpret_cast<uint16_t*>(pw);               // bf16 probabilities
   const uint32_t* pw2 = reinterpret_cast<const uint32_t*>(pw);   // ... as token pairs
@@ -947,8 +1005,9 @@ __global__ __launch_bounds__(256) void valu_attn(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
       if (r >= R) continue;
-      const int lim = t.L - a.q_len + r / a.group;
-      const float v = (in && blk_ok && tok <= lim) ? sc[r] : -INFINITY;
+      const int off = tok - ctx_end;
+      const bool vis = off < 0 || ((vbits[r] >> (off & 31)) & 1u);
+      const float v = (in && blk_ok && vis) ? sc[r] : -INFINITY;
       float mx = v;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
@@ -1125,6 +1184,7 @@ struct Plan {
   int path, sched, part_tokens, parts, waves, grid, merge_grid, nt, rows;
   bool stream;  // K/V loads with the non-temporal hint
   bool kv8;     // FP8 pools
+  bool tree;    // per-row visibility masks over the drafted positions
   int64_t segments, pieces;  // balanced schedule: segments, partial slots
   size_t ws;
 };
@@ -1179,6 +1239,7 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   pl->rows = int(rows);
   pl->stream = d->kv_shared == 0;
   pl->kv8 = d->kv_format == PA_KV_FP8_E4M3;
+  pl->tree = false;  // set by the tree entry point
   const bool balanced = path == PA_PATH_MFMA && d->partition_tokens == 0 &&
                         d->num_seqs <= kMaxBalancedSeqs;
   if (balanced) {
@@ -1247,17 +1308,23 @@ int resident_groups(const void* kernel, int threads, size_t lds) {
 }
 
 // The main kernel a plan launches (one template instance per shape).
-template <int D, int BS, int NT, bool STREAM, bool KV8>
+template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE>
 const void* mfma_kernel(bool balanced) {
-  return balanced ? reinterpret_cast<const void*>(mfma_attn_balanced<D, BS, NT, STREAM, KV8>)
-                  : reinterpret_cast<const void*>(mfma_attn<D, BS, NT, STREAM, KV8>);
+  return balanced ? reinterpret_cast<const void*>(mfma_attn_balanced<D, BS, NT, STREAM, KV8, TREE>)
+                  : reinterpret_cast<const void*>(mfma_attn<D, BS, NT, STREAM, KV8, TREE>);
+}
+
+template <int D, int BS, int NT, bool TREE>
+const void* mfma_kernel(const Plan& pl) {
+  const bool bal = pl.sched == PA_SCHED_BALANCED;
+  if (pl.kv8)
+    return pl.stream ? mfma_kernel<D, BS, NT, true, true, TREE>(bal) : mfma_kernel<D, BS, NT, false, true, TREE>(bal);
+  return pl.stream ? mfma_kernel<D, BS, NT, true, false, TREE>(bal) : mfma_kernel<D, BS, NT, false, false, TREE>(bal);
 }
 
 template <int D, int BS, int NT>
 const void* mfma_kernel(const Plan& pl) {
-  const bool bal = pl.sched == PA_SCHED_BALANCED;
-  if (pl.kv8) return pl.stream ? mfma_kernel<D, BS, NT, true, true>(bal) : mfma_kernel<D, BS, NT, false, true>(bal);
-  return pl.stream ? mfma_kernel<D, BS, NT, true, false>(bal) : mfma_kernel<D, BS, NT, false, false>(bal);
+  return pl.tree ? mfma_kernel<D, BS, NT, true>(pl) : mfma_kernel<D, BS, NT, false>(pl);
 }
 
 template <int D, int BS>
@@ -1286,9 +1353,9 @@ pa_status launch_main(const Plan& pl, const pa_attn_desc* d, const AttnArgs& arg
   const size_t lds = lds_bytes(pl, d->head_dim, d->num_seqs);
   const int grid = launch_grid(pl, d);
   void* kargs[] = {const_cast<AttnArgs*>(&args)};
-  if (hipLaunchKernel(k, dim3(grid), dim3(64 * pl.waves), kargs, lds, s) != hipSuccess) {
+  if (const hipError_t e = hipLaunchKernel(k, dim3(grid), dim3(64 * pl.waves), kargs, lds, s); e != hipSuccess) {
     (void)hipGetLastError();
-    return PA_ERR_HIP;
+    return pa::hip_failed(e);
   }
   return PA_OK;
 }
@@ -1300,7 +1367,8 @@ pa_status launch_merge(const Plan& pl, int dtype, const AttnArgs& args, hipStrea
     hipLaunchKernelGGL((lse_merge<float, D>), dim3(pl.merge_grid), block, 0, s, args);
   else
     hipLaunchKernelGGL((lse_merge<uint16_t, D>), dim3(pl.merge_grid), block, 0, s, args);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : pa::hip_failed(e);
 }
 
 }  // namespace
@@ -1326,14 +1394,17 @@ extern "C" size_t pa_attention_workspace_size(const pa_attn_desc* desc, int32_t 
   return make_plan(desc, q_len, &pl) == PA_OK ? pl.ws : 0;
 }
 
-extern "C" pa_status pa_attention(const pa_attn_desc* desc, const void* q, const void* k_pool,
-                                  const void* v_pool, const int32_t* block_tables,
-                                  const int32_t* context_lens, int32_t q_len, float scale,
-                                  void* out, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+namespace {
+
+pa_status attention_impl(const pa_attn_desc* desc, const void* q, const void* k_pool,
+                         const void* v_pool, const int32_t* block_tables,
+                         const int32_t* context_lens, int32_t q_len, const uint32_t* tree_mask,
+                         int32_t mask_stride, float scale, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   Plan pl;
   pa_status st = make_plan(desc, q_len, &pl);
   if (st != PA_OK) return st;
+  pl.tree = tree_mask != nullptr;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
     return PA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
@@ -1350,6 +1421,8 @@ extern "C" pa_status pa_attention(const pa_attn_desc* desc, const void* q, const
   args.part_o = nullptr;
   args.k_scales = nullptr;
   args.v_scales = nullptr;
+  args.tree_mask = tree_mask;
+  args.mask_stride = mask_stride;
   if (pl.kv8) {
     const int64_t codes = pa::fp8_codes_bytes(desc->num_blocks, desc->num_kv_heads, desc->block_size,
                                               desc->head_dim);
@@ -1384,4 +1457,28 @@ extern "C" pa_status pa_attention(const pa_attn_desc* desc, const void* q, const
   if (st != PA_OK || pl.merge_grid == 0) return st;
   return desc->head_dim == 64 ? launch_merge<64>(pl, desc->dtype, args, s)
                               : launch_merge<128>(pl, desc->dtype, args, s);
+}
+
+}  // namespace
+
+extern "C" pa_status pa_attention(const pa_attn_desc* desc, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* block_tables,
+                                  const int32_t* context_lens, int32_t q_len, float scale,
+                                  void* out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return attention_impl(desc, q, k_pool, v_pool, block_tables, context_lens, q_len, nullptr, 0,
+                        scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" pa_status pa_attention_tree(const pa_attn_desc* desc, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_tables,
+                                       const int32_t* context_lens, int32_t q_len,
+                                       const uint32_t* tree_mask, int32_t mask_stride, float scale,
+                                       void* out, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (!tree_mask || q_len < 1 || q_len > PA_TREE_MAX_NODES) return PA_ERR_INVALID_ARG;
+  if (mask_stride != 0 && mask_stride < q_len) return PA_ERR_INVALID_ARG;
+  if (desc && int64_t(mask_stride) * (desc->num_seqs - 1) + q_len > INT32_MAX) return PA_ERR_INVALID_ARG;
+  return attention_impl(desc, q, k_pool, v_pool, block_tables, context_lens, q_len, tree_mask,
+                        mask_stride, scale, out, workspace, workspace_bytes, stream);
 }

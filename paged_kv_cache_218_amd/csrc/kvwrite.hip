@@ -173,7 +173,7 @@ pa_status launch_copies(const pa_pool* p, void* k_pool, void* v_pool, const int3
     }
     hipLaunchKernelGGL(copy_blocks_kernel<T>, dim3(gx, n), dim3(threads), 0, stream,
                        static_cast<T*>(k_pool), static_cast<T*>(v_pool), cp, block_elems);
-    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    if (const hipError_t e = hipGetLastError(); e != hipSuccess) return pa::hip_failed(e);
   }
   return PA_OK;
 }
@@ -217,7 +217,7 @@ pa_status launch_scatter_fp8(const pa_pool* p, void* k_pool, void* v_pool, const
     else
       hipLaunchKernelGGL(scatter_fp8_kernel<128>, dim3(grid), dim3(threads), 0, stream, kc, vc, ksc, vsc, kn,
                          vn, ids, lb, pos0, pos0 - start_pos, n, hkv, bs);
-    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    if (const hipError_t e = hipGetLastError(); e != hipSuccess) return pa::hip_failed(e);
   }
   return PA_OK;
 }
@@ -244,7 +244,7 @@ pa_status launch_scatter(const pa_pool* p, void* k_pool, void* v_pool, const int
                        static_cast<T*>(k_pool), static_cast<T*>(v_pool),
                        static_cast<const T*>(k_new), static_cast<const T*>(v_new), ids, lb,
                        pos0, pos0 - start_pos, n, hkv, d, bs);
-    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    if (const hipError_t e = hipGetLastError(); e != hipSuccess) return pa::hip_failed(e);
   }
   return PA_OK;
 }

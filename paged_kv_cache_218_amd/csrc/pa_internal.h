@@ -29,6 +29,10 @@ inline int64_t fp8_codes_bytes(int64_t num_blocks, int64_t hkv, int64_t bs, int6
   return num_blocks * hkv * bs * d;
 }
 
+// Record a failed HIP call (this thread's last one, read by pa_last_hip_error)
+// and return PA_ERR_HIP. Defined with the HIP sources.
+pa_status hip_failed(int hip_error);
+
 // Host planning of a write (allocation on growth, copy-on-write on shared
 // blocks). copies receives (src, dst) pairs; slots may be null.
 pa_status plan_write(pa_pool* p, int32_t* table, int32_t capacity, int32_t* live_inout,

@@ -219,3 +219,16 @@ extern "C" pa_status pa_write_plan(pa_pool* pool, int32_t* block_table, int32_t 
   if (copies_out && n) std::memcpy(copies_out, copies.data(), copies.size() * sizeof(int32_t));
   return PA_OK;
 }
+
+// Ancestor masks of a tree of drafted tokens: bit j of masks[i] is set when
+// node j is node i or one of its ancestors (a candidate token sees the
+// candidates it continues; speculative decoding variants, parallel decoding of
+// a candidate tree, in "Mở rộng Quy mô và Triển khai", "Giải mã Suy đoán").
+extern "C" pa_status pa_tree_masks(const int32_t* parents, int32_t n, uint32_t* masks) {
+  if (!parents || !masks || n < 1 || n > PA_TREE_MAX_NODES) return PA_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    if (parents[i] < -1 || parents[i] >= i) return PA_ERR_INVALID_ARG;  // parents come first
+  for (int32_t i = 0; i < n; ++i)
+    masks[i] = (uint32_t(1) << i) | (parents[i] >= 0 ? masks[parents[i]] : 0u);
+  return PA_OK;
+}

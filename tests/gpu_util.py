@@ -26,7 +26,7 @@ def out_bits(t):
 
 
 def run_gpu(w, path=0, partition_tokens=0, shared_prefix=True, cache=None, q=None, lens=None,
-            max_context=None, waves=0):
+            max_context=None, waves=0, tree_mask=None, mask_stride=None):
     import torch
     from paged_kv_cache_218_amd.cache import PagedKVCache, lens_to_device, queries_to_device
     cfg = w.cfg
@@ -36,7 +36,7 @@ def run_gpu(w, path=0, partition_tokens=0, shared_prefix=True, cache=None, q=Non
     lens_d = lens_to_device(w) if lens is None else lens
     out = cache.attention(q, cache.tables_device(), lens_d, cfg.q_len, cfg.scale,
                           max_context or int(w.lens.max()), path=path, partition_tokens=partition_tokens,
-                          waves_per_group=waves)
+                          waves_per_group=waves, tree_mask=tree_mask, mask_stride=mask_stride)
     torch.cuda.synchronize()
     return out, cache
 
@@ -59,6 +59,12 @@ def oracle_rows(w, seqs):
             k = fp8.dequantize(*fp8.quantize_rows(to_f64(k, "bf16").astype(np.float32)))
             v = fp8.dequantize(*fp8.quantize_rows(to_f64(v, "bf16").astype(np.float32)))
             kv_dtype = "f64"
+        if w.tree_parents is not None:
+            from oracle import tree as otree
+            res[b] = otree.attention_tree_contiguous(w.seqs[b].q, k, v, cfg.q_len, cfg.num_q_heads,
+                                                     cfg.num_kv_heads, otree.ancestor_masks(w.tree_parents[b]),
+                                                     cfg.scale, cfg.dtype, kv_dtype)
+            continue
         res[b] = oatt.attention_contiguous(w.seqs[b].q, k, v, cfg.q_len, cfg.num_q_heads,
                                            cfg.num_kv_heads, cfg.scale, cfg.dtype, kv_dtype)
     return res

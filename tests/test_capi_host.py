@@ -245,3 +245,51 @@ def test_attention_plan_validation():
     assert (pl.num_partitions, pl.merge_grid) == (256, 4 * 64)
     assert pl.workspace_bytes == 4 * 64 * 256 * (128 + 2) * 4
     assert pa.pa_attention_workspace_size(d, 1) == pl.workspace_bytes
+
+
+def test_tree_masks_bit_exact_vs_oracle():
+    from oracle import tree as otree
+    rng = np.random.default_rng(11)
+    for n in (1, 2, 5, 8, 17, 32):
+        for _ in range(20):
+            parents = [int(rng.integers(-1, j)) for j in range(n)]
+            got = pa.pa_tree_masks(np.array(parents, dtype=np.int32))
+            assert got.tolist() == otree.ancestor_masks(parents)
+
+
+@pytest.mark.parametrize("bad", [[0], [-1, 1], [-1, 2, 0], [-2], list(range(-1, 32))])
+def test_tree_masks_errors(bad):
+    with pytest.raises(pa.PAError) as ex:
+        pa.pa_tree_masks(np.array(bad, dtype=np.int32))
+    assert ex.value.status == _lib.PA_ERR_INVALID_ARG
+
+
+def test_attention_tree_rejects_bad_masks_before_launch():
+    """Argument checks of the tree entry point return before any device work
+    (the pointers below are never dereferenced)."""
+    import ctypes as C
+    desc = pa.make_desc(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                        max_blocks_per_seq=8, num_blocks=32, dtype=pa.PA_DTYPE_BF16, max_context=128)
+    fake = 256
+
+    def call(q_len, mask, stride):
+        return _lib.lib.pa_attention_tree(C.byref(desc), fake, fake, fake, fake, fake, q_len, mask, stride,
+                                          1.0, fake, None, 0, None)
+    assert call(4, None, 4) == _lib.PA_ERR_INVALID_ARG          # no masks
+    assert call(33, fake, 33) == _lib.PA_ERR_INVALID_ARG        # more nodes than mask bits
+    assert call(4, fake, 3) == _lib.PA_ERR_INVALID_ARG          # rows of one sequence overlap the next
+    assert call(4, fake, -1) == _lib.PA_ERR_INVALID_ARG
+    assert call(0, fake, 0) == _lib.PA_ERR_INVALID_ARG
+
+
+def test_one_hip_runtime_per_process():
+    """Importing the package before torch must not load a second HIP runtime."""
+    import subprocess
+    import sys
+    code = ("import paged_kv_cache_218_amd, torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "1"

@@ -1,4 +1,4 @@
-"""The five workloads at full size on the GPU, in the launch configuration the
+"""The workloads at full size on the GPU, in the launch configuration the
 bench times: sampled sequences against the oracle, tables bit-exact."""
 import numpy as np
 import pytest
@@ -12,7 +12,8 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 from tests.gpu_util import assert_close, oracle_rows, out_to_f64, run_gpu  # noqa: E402
 
 SAMPLE = {"tiny_f32": None, "llama3_8b_decode": [0, 17, 63], "llama3_70b_decode": [0, 41],
-          "prefix_verify": [0, 64, 127], "long_ctx_split": [3], "llama3_70b_decode_fp8": [0, 63]}
+          "prefix_verify": [0, 64, 127], "long_ctx_split": [3], "llama3_70b_decode_fp8": [0, 63],
+          "tree_verify": [0, 77, 127]}
 
 
 def model_tables(w):
@@ -40,7 +41,11 @@ def test_full_size(name):
     cfg = workloads.CONFIGS[name]
     print(f"full-size {name}", flush=True)
     w = workloads.generate(cfg, threads=16)
-    out, cache = run_gpu(w, partition_tokens=cfg.partition_tokens)
+    masks = None
+    if w.tree_parents is not None:
+        from paged_kv_cache_218_amd.cache import tree_masks_to_device
+        masks = tree_masks_to_device(w.tree_parents)
+    out, cache = run_gpu(w, partition_tokens=cfg.partition_tokens, tree_mask=masks)
     tabs, m = model_tables(w)
     assert np.array_equal(cache.tables, tabs)
     assert [pa.pa_block_refcount(cache.pool, b) for b in range(w.num_blocks)] == m.refcount

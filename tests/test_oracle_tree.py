@@ -135,3 +135,16 @@ def test_tree_rows_independent_of_other_branches():
         for i in range(cfg.q_len):
             changed = not np.array_equal(out[0, i], base[0, i])
             assert changed == bool((masks[0][i] >> j) & 1), (i, j)
+
+
+def test_contiguous_form_equals_paged_form():
+    w = tree_workload()
+    cfg = w.cfg
+    pool, _, tables, _ = build_pool(w)
+    masks = masks_of(w)
+    paged = otree.attention_tree(w.q_all(), pool, tables, w.lens, cfg.q_len, masks, cfg.scale)
+    for b in range(cfg.batch):
+        k, v = w.logical_kv(b)
+        flat = otree.attention_tree_contiguous(w.seqs[b].q, k, v, cfg.q_len, cfg.num_q_heads, cfg.num_kv_heads,
+                                               masks[b], cfg.scale, cfg.dtype)
+        assert np.array_equal(flat, paged[b])
