@@ -97,7 +97,7 @@ def kernel_name(cfg, plan, desc) -> str:
         t = "float" if cfg.dtype == "f32" else "unsigned short"
         return f"valu_attn<{t}, {cfg.head_dim}, {cfg.block_size}>"
     base = "mfma_attn_balanced" if plan.schedule == 1 else "mfma_attn"
-    nt = 2 if cfg.group * cfg.q_len > 16 else 1
+    nt = plan.tiles_per_wave
     stream = "false" if desc.kv_shared else "true"
     kv8 = "true" if desc.kv_format else "false"
     tree = "true" if cfg.tree else "false"
@@ -310,7 +310,7 @@ def main():
             "path": path_name, "partition_tokens": plan.partition_tokens,
             "schedule": {0: "partitions", 1: "balanced"}[plan.schedule], "kv_shared": int(desc.kv_shared),
             "partitions": plan.num_partitions, "waves_per_group": plan.waves_per_group,
-            "grid": plan.grid, "merge_grid": plan.merge_grid,
+            "grid": plan.grid, "merge_grid": plan.merge_grid, "tiles_per_wave": plan.tiles_per_wave,
         },
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(tokens, 1),

@@ -246,6 +246,8 @@ typedef struct pa_attn_plan {
                                  capacity of the current device for that kernel (an
                                  upper bound when no device is available) */
   int32_t merge_grid;         /* workgroups of the merge kernel (0 if none) */
+  int32_t tiles_per_wave;     /* MFMA: 16-row query tiles each wavefront holds (1, or 2
+                                 when G*q_len > 16); 0 for the VALU path */
   size_t workspace_bytes;     /* workspace pa_attention needs */
 } pa_attn_plan;
 

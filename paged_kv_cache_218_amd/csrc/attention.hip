@@ -125,6 +125,28 @@ __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 64- and 128-bit accesses with the same coherence (the sc1 cache policy) for
+// the balanced schedule's partials, through buffer resources over one
+// piece's (or one segment's) partials; out-of-range accesses read zero and
+// write nothing.
+constexpr int kCoherent = 16;  // sc1 cache-policy bit
+constexpr int kRawBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, int(bytes), kRawBufferWord3);
+}
+__device__ __forceinline__ f32x4 load4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, kCoherent));
+}
+__device__ __forceinline__ f32x2 load2_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, int(off), 0, kCoherent));
+}
+__device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, int(off), 0, kCoherent);
+}
+__device__ __forceinline__ void store2_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, int(off), 0, kCoherent);
+}
+
 // Decode the workgroup id. Returns false when the partition is empty.
 struct Tile {
   int b, g, part, L, t0, t1;
@@ -720,6 +742,114 @@ __device__ __forceinline__ int64_t owner(int64_t x, int64_t S, int64_t N) {
   return k;
 }
 
+// LDS floats the merge of a segment's pieces needs beyond the R x D output
+// accumulators (it reuses the park area): per-row partial maxima and sums of
+// up to 8 thread groups, the rows' final ones and a chunk of piece weights.
+constexpr int kMergeChunk = 64;  // pieces whose weights sit in LDS at once
+constexpr int kMergeLdsFloats = 2 * 8 * 32 + 2 * 32 + kMergeChunk * 32;
+constexpr int kMergeBatch = 8;   // partial loads in flight per thread
+#ifndef PA_MIN_GROUP_STEPS
+#define PA_MIN_GROUP_STEPS 8
+#endif
+constexpr int kMinGroupSteps = PA_MIN_GROUP_STEPS;  // fewest steps a workgroup's range holds
+
+// The workgroup that completed a segment merges its npieces partials, which
+// start at piece p0 (log-sum-exp identity: M = max m_p, w_p = l_p 2^(m_p - M),
+// out = sum_p w_p o_p / sum_p w_p). The (m, l) pairs are folded by thread
+// groups into online (max, sum) per row; the weighted sums of o run over
+// 4-column chunks with kMergeBatch independent loads in flight. out0: the
+// segment's first output row.
+template <int D>
+__device__ void merge_pieces(const AttnArgs& a, int64_t p0, int npieces, int R, uint16_t* out0,
+                             float* lds) {
+  // The opaque copy keeps the thread-index arithmetic below inside this
+  // function: hoisted out of the caller's loop it would stay live across
+  // the attention steps and cost registers there.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int T = blockDim.x;
+  const int QN = min(8, T / 32);   // thread groups per row for the row statistics
+  float* red_m = lds;              // [8][32]
+  float* red_l = red_m + 8 * 32;   // [8][32]
+  float* row_M = red_l + 8 * 32;   // [32]
+  float* row_den = row_M + 32;     // [32]
+  float* wts = row_den + 32;       // [kMergeChunk][32]
+  f32x4* acc_s = reinterpret_cast<f32x4*>(wts + kMergeChunk * 32);  // [R * D / 4]
+  const auto ml_r = partial_rsrc(a.part_ml + p0 * R * 2, uint32_t(npieces) * R * 8);
+  const auto o_r = partial_rsrc(a.part_o + p0 * R * D, uint32_t(npieces) * R * D * 4);
+  const int nc = R * D / 4;
+  for (int e = tid; e < nc; e += T) acc_s[e] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // row statistics: thread (q, r) folds pieces q, q + QN, ... of row r
+  {
+    const int r = tid % 32, q = tid / 32;
+    float m_run = -INFINITY, l_run = 0.f;
+    if (r < R && q < QN) {
+      for (int p = q; p < npieces; p += 4 * QN) {
+        f32x2 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = load2_coherent(ml_r, uint32_t((p + QN * u) * R + r) * 8);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (p + QN * u < npieces) {
+            const float m_new = fmaxf(m_run, v[u][0]);
+            const float mu = m_new == -INFINITY ? 0.f : m_new;
+            l_run = l_run * fast_exp2(m_run - mu) + v[u][1] * fast_exp2(v[u][0] - mu);
+            m_run = m_new;
+          }
+        }
+      }
+      red_m[q * 32 + r] = m_run;
+      red_l[q * 32 + r] = l_run;
+    }
+    __syncthreads();
+    if (tid < R) {
+      float M = -INFINITY;
+      for (int qq = 0; qq < QN; ++qq) M = fmaxf(M, red_m[qq * 32 + tid]);
+      const float mu = M == -INFINITY ? 0.f : M;
+      float den = 0.f;
+      for (int qq = 0; qq < QN; ++qq) den += red_l[qq * 32 + tid] * fast_exp2(red_m[qq * 32 + tid] - mu);
+      row_M[tid] = mu;
+      row_den[tid] = den;
+    }
+    __syncthreads();
+  }
+  // weighted sums, kMergeChunk pieces at a time (uniform loop: every thread
+  // reaches every barrier)
+  for (int pc = 0; pc < npieces; pc += kMergeChunk) {
+    const int n = min(kMergeChunk, npieces - pc);
+    for (int e = tid; e < n * R; e += T) {
+      const int pp = e / R, rr = e % R;
+      const f32x2 v = load2_coherent(ml_r, uint32_t((pc + pp) * R + rr) * 8);
+      wts[pp * 32 + rr] = v[1] * fast_exp2(v[0] - row_M[rr]);
+    }
+    __syncthreads();
+    for (int ch = tid; ch < nc; ch += T) {
+      const int r = ch / (D / 4), c = 4 * (ch % (D / 4));
+      f32x4 acc = acc_s[ch];
+      for (int p = 0; p < n; p += kMergeBatch) {
+        f32x4 o[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u)
+          o[u] = load4_coherent(o_r, uint32_t(((pc + p + u) * R + r) * D + c) * 4);
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u)
+          if (p + u < n) acc += wts[(p + u) * 32 + r] * o[u];
+      }
+      acc_s[ch] = acc;
+    }
+    __syncthreads();
+  }
+  for (int ch = tid; ch < nc; ch += T) {
+    const int r = ch / (D / 4), c = 4 * (ch % (D / 4));
+    const float den = row_den[r];
+    const f32x4 acc = acc_s[ch];
+    const int i = r / a.group, hh = r % a.group;  // drafted token, head within the group
+    uint16_t* dst = out0 + (int64_t(i) * a.hq + hh) * D + c;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) store_f<uint16_t>(dst + u, den > 0.f ? acc[u] / den : NAN);
+  }
+}
+
 template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE>
 __global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
   extern __shared__ float smem[];  // [B+1] step prefix sums, then the parked states
@@ -771,7 +901,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
   // With no more workgroups than steps every range is non-empty, so the
   // pieces of a segment are exactly the workgroups from its first owner to
   // its last.
-  const int64_t N = min(int64_t(gridDim.x), S);
+  const int64_t N = min(int64_t(gridDim.x), (S + kMinGroupSteps - 1) / kMinGroupSteps);
   if (k >= N) return;
   const int64_t x0 = range_start(k, S, N), x1 = range_start(k + 1, S, N);
   // first sequence whose segments reach past x0
@@ -784,6 +914,11 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
     }
     b = lo;
   }
+  __shared__ int64_t duty_seg[2], duty_p0[2];
+  __shared__ int duty_n[2];
+  __shared__ int n_duty;
+  if (threadIdx.x == 0) n_duty = 0;
+  __syncthreads();
   int64_t x = x0;
   while (x < x1) {
     int nb = pre[b + 1] - pre[b];
@@ -809,15 +944,22 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
       }
     } else {
       const int64_t piece = k + seg;
-      for (int e = threadIdx.x; e < R * D; e += blockDim.x) {
-        const int r = e / D, c = e % D;
-        float M, l, o;
-        combine_waves(park, W, R, D, r, c, M, l, o);
-        store_coherent(&a.part_o[(piece * R + r) * D + c], bad ? NAN : o);
-        if (c == 0) {
-          store_coherent(&a.part_ml[(piece * R + r) * 2 + 0], bad ? NAN : M);
-          store_coherent(&a.part_ml[(piece * R + r) * 2 + 1], bad ? NAN : l);
+      // this piece's (m, l) per row and o per row, 4 columns per store
+      const auto ml_r = partial_rsrc(a.part_ml + piece * R * 2, uint32_t(R) * 8);
+      const auto o_r = partial_rsrc(a.part_o + piece * R * D, uint32_t(R) * D * 4);
+      for (int e = threadIdx.x; e < R * D / 4; e += blockDim.x) {
+        const int r = e / (D / 4), c = 4 * (e % (D / 4));
+        f32x4 v;
+        float M, l;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float o;
+          combine_waves(park, W, R, D, r, c + u, M, l, o);
+          v[u] = o;
         }
+        if (bad) v = (f32x4){NAN, NAN, NAN, NAN};
+        store4_coherent(o_r, uint32_t(r * D + c) * 4, v);
+        if (c == 0) store2_coherent(ml_r, uint32_t(r) * 8, bad ? (f32x2){NAN, NAN} : (f32x2){M, l});
       }
       // Every wave waits until its partial stores are complete at the
       // coherent level, then one thread counts the piece in. The workgroup
@@ -831,49 +973,26 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
       if (threadIdx.x == 0)
         arrived = __hip_atomic_fetch_add(&a.counters[seg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
-      if (arrived == npieces - 1) {
-        const int64_t p0 = k_first + seg;
-        // per row: global maximum and weight sum (rows spread over the threads)
-        __shared__ float row_M[kMfmaMaxRows], row_den[kMfmaMaxRows];
-        for (int r = threadIdx.x; r < R; r += blockDim.x) {
-          float M = -INFINITY;
-          for (int p = 0; p < npieces; ++p) M = fmaxf(M, load_coherent(&a.part_ml[((p0 + p) * R + r) * 2]));
-          const float Mu = (M == -INFINITY) ? 0.f : M;
-          float den = 0.f;
-          for (int p = 0; p < npieces; ++p) {
-            const int64_t pr = (p0 + p) * R + r;
-            den += load_coherent(&a.part_ml[pr * 2 + 1]) * fast_exp2(load_coherent(&a.part_ml[pr * 2]) - Mu);
-          }
-          row_M[r] = Mu;
-          row_den[r] = den;
-        }
-        __syncthreads();
-        for (int e = threadIdx.x; e < R * D; e += blockDim.x) {
-          const int r = e / D, c = e % D;
-          const float Mu = row_M[r];
-          float num0 = 0.f, num1 = 0.f;
-          int p = 0;
-          for (; p + 1 < npieces; p += 2) {
-            const int64_t pr0 = (p0 + p) * R + r, pr1 = pr0 + R;
-            const float w0 = load_coherent(&a.part_ml[pr0 * 2 + 1]) * fast_exp2(load_coherent(&a.part_ml[pr0 * 2]) - Mu);
-            const float w1 = load_coherent(&a.part_ml[pr1 * 2 + 1]) * fast_exp2(load_coherent(&a.part_ml[pr1 * 2]) - Mu);
-            num0 = fmaf(w0, load_coherent(&a.part_o[pr0 * D + c]), num0);
-            num1 = fmaf(w1, load_coherent(&a.part_o[pr1 * D + c]), num1);
-          }
-          if (p < npieces) {
-            const int64_t pr = (p0 + p) * R + r;
-            num0 = fmaf(load_coherent(&a.part_ml[pr * 2 + 1]) * fast_exp2(load_coherent(&a.part_ml[pr * 2]) - Mu),
-                        load_coherent(&a.part_o[pr * D + c]), num0);
-          }
-          const float den = row_den[r];
-          store_f<uint16_t>(out + int64_t(out_row(a, b, g, r)) * D + c, den > 0.f ? (num0 + num1) / den : NAN);
-        }
-        if (threadIdx.x == 0)  // ready for the next call
-          __hip_atomic_store(&a.counters[seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (arrived == npieces - 1 && threadIdx.x == 0) {  // this workgroup merges the segment
+        duty_seg[n_duty] = seg;
+        duty_p0[n_duty] = k_first + seg;
+        duty_n[n_duty] = npieces;
+        ++n_duty;
       }
     }
     __syncthreads();  // the park area is reused by the next piece
     x = seg_start + last;
+  }
+  // Merges after the steps (only a range's first and last piece can be
+  // partial, so at most two), kept out of the step loop's registers.
+  for (int d = 0; d < n_duty; ++d) {
+    const int64_t seg = duty_seg[d];
+    const int bb = int(seg / a.hkv), gg = int(seg % a.hkv);
+    merge_pieces<D>(a, duty_p0[d], duty_n[d], R,
+                    static_cast<uint16_t*>(a.out) + int64_t(out_row(a, bb, gg, 0)) * D, park);
+    if (threadIdx.x == 0)  // ready for the next call
+      __hip_atomic_store(&a.counters[seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
   }
 }
 
@@ -1288,7 +1407,9 @@ size_t lds_bytes(const Plan& pl, int D, int num_seqs) {
   if (pl.path == PA_PATH_MFMA) {
     const size_t park = size_t(pl.waves) * pl.rows * (D + 2) * sizeof(float);
     if (pl.sched == PA_SCHED_PARTITIONS) return park;
-    return size_t((num_seqs + 1 + 3) & ~3) * sizeof(int32_t) + park;
+    // the park area also holds the merge of a segment's pieces
+    const size_t merge = (size_t(kMergeLdsFloats) + size_t(pl.rows) * D) * sizeof(float);
+    return size_t((num_seqs + 1 + 3) & ~3) * sizeof(int32_t) + std::max(park, merge);
   }
   const size_t first = size_t(kValuMaxRows) * D + size_t(pl.waves) * kValuMaxRows * 64;
   const size_t merge = size_t(pl.waves) * kValuMaxRows * (D + 2);
@@ -1385,6 +1506,7 @@ extern "C" pa_status pa_attention_plan(const pa_attn_desc* desc, int32_t q_len, 
   out->waves_per_group = pl.waves;
   out->grid = launch_grid(pl, desc);
   out->merge_grid = pl.merge_grid;
+  out->tiles_per_wave = pl.path == PA_PATH_MFMA ? pl.nt : 0;
   out->workspace_bytes = pl.ws;
   return PA_OK;
 }
