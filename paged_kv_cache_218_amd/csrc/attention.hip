@@ -319,9 +319,10 @@ __device__ __forceinline__ void wave_state_init(WaveState<D, NT>& st) {
 // One wavefront's share of a piece: steps first, first+W, ... < end of
 // sequence b (context L), KV head g. Every step covers 32 tokens; tokens at
 // or past L, and tokens after a row's causal limit, are masked.
-template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE>
-__device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int first, int end, int W,
-                                WaveState<D, NT>& st) {
+// next_step(s) gives the wave's step after s (>= end: none left).
+template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE, typename NextStep>
+__device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int first, int end,
+                                WaveState<D, NT>& st, NextStep next_step) {
   constexpr int KS = D / 32;  // k-steps over the head dim for QK
   constexpr int DT = D / 16;  // 16-row tiles of the head dim for PV
   const int lane = threadIdx.x % 64;
@@ -523,7 +524,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
       }
     };
     StepBuf8<D> buf;
-    for (int s = first; s < end; s += W) {
+    for (int s = first; s < end; s = next_step(s)) {
       load_step8(buf, s);
       compute_step8(buf);
     }
@@ -647,7 +648,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     // fit) hide this wave's load latency. (A two-buffer ping-pong was measured
     // no faster: the extra registers cost a wave per SIMD.)
     StepBuf<D> buf;
-    for (int s = first; s < end; s += W) {
+    for (int s = first; s < end; s = next_step(s)) {
       load_step(buf, s);
       compute_step(buf);
     }
@@ -719,7 +720,8 @@ __global__ __launch_bounds__(256, 2) void mfma_attn(AttnArgs a) {
   WaveState<D, NT> st;
   wave_state_init(st);
   const int s0 = t.t0 / kStep, s1 = (t.t1 + kStep - 1) / kStep;
-  mfma_wave_steps<D, BS, NT, STREAM, KV8, TREE>(a, t.b, t.g, t.L, s0 + wave, s1, W, st);
+  mfma_wave_steps<D, BS, NT, STREAM, KV8, TREE>(a, t.b, t.g, t.L, s0 + wave, s1, st,
+                                                [W](int s) { return s + W; });
   const bool bad = park_states(st, R, smem);
   merge_and_store<uint16_t, D>(a, t, R, R, W, smem, smem + W * R, smem + 2 * W * R, bad);
 }
@@ -850,8 +852,12 @@ __device__ void merge_pieces(const AttnArgs& a, int64_t p0, int npieces, int R, 
   }
 }
 
+// Resident waves per compute unit for NT row tiles (registers allow three
+// waves per SIMD with one tile, two with two).
+constexpr int balanced_waves(int nt) { return nt == 1 ? 12 : 8; }
+
 template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE>
-__global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
+__global__ __launch_bounds__(64 * balanced_waves(NT)) void mfma_attn_balanced(AttnArgs a) {
   extern __shared__ float smem[];  // [B+1] step prefix sums, then the parked states
   const int W = blockDim.x / 64, wave = threadIdx.x / 64;
   const int R = a.group * a.q_len;
@@ -876,7 +882,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
       const int v = __shfl_up(incl, o);
       if ((tid & 63) >= o) incl += v;
     }
-    __shared__ int wave_tot[4];
+    __shared__ int wave_tot[16];  // one per wavefront (at most 1024 threads)
     if ((tid & 63) == 63) wave_tot[tid >> 6] = incl;
     __syncthreads();
     int run = incl - local;
@@ -930,7 +936,8 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_balanced(AttnArgs a) {
     const int L = a.lens[b];
     WaveState<D, NT> st;
     wave_state_init(st);
-    mfma_wave_steps<D, BS, NT, STREAM, KV8, TREE>(a, b, g, L, first + wave, last, W, st);
+    mfma_wave_steps<D, BS, NT, STREAM, KV8, TREE>(a, b, g, L, first + wave, last, st,
+                                                  [W](int s) { return s + W; });
     const bool bad = park_states(st, R, park);
     const int64_t seg = int64_t(b) * a.hkv + g;
     const bool whole = first == 0 && last == nb;
@@ -1313,6 +1320,35 @@ constexpr int kMaxBalancedSeqs = 8192;  // step prefix sums live in LDS
 int ceil_div(int64_t x, int64_t y) { return int((x + y - 1) / y); }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS of one compute unit (gfx950)
+constexpr int kPerCuMinContext = 6144;  // longest context at which one workgroup per CU pays
+
+size_t lds_bytes(const Plan& pl, int D, int num_seqs) {
+  if (pl.path == PA_PATH_MFMA) {
+    const size_t park = size_t(pl.waves) * pl.rows * (D + 2) * sizeof(float);
+    if (pl.sched == PA_SCHED_PARTITIONS) return park;
+    // the park area also holds the merge of a segment's pieces
+    const size_t merge = (size_t(kMergeLdsFloats) + size_t(pl.rows) * D) * sizeof(float);
+    return size_t((num_seqs + 1 + 3) & ~3) * sizeof(int32_t) + std::max(park, merge);
+  }
+  const size_t first = size_t(kValuMaxRows) * D + size_t(pl.waves) * kValuMaxRows * 64;
+  const size_t merge = size_t(pl.waves) * kValuMaxRows * (D + 2);
+  return std::max(first, merge) * sizeof(float);
+}
+
+// Default wavefronts per workgroup. Balanced schedule with long contexts:
+// one workgroup per compute unit holding every resident wave, so the
+// compute unit's waves share one range (workgroups dispatched earlier on a
+// compute unit otherwise run ahead of the later ones and finish early). With
+// shorter contexts the ranges hold more segment boundaries, where all of a
+// workgroup's waves wait for its slowest one, and three workgroups of four
+// waves per compute unit keep each other's gaps filled.
+int default_waves(const Plan& pl, int max_context) {
+  if (pl.sched == PA_SCHED_BALANCED && pl.nt == 1 && max_context >= kPerCuMinContext)
+    return balanced_waves(pl.nt);
+  return 4;
+}
+
 pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   if (!d || !pl) return PA_ERR_INVALID_ARG;
   for (int k = 0; k < 2; ++k)
@@ -1320,7 +1356,7 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   if (d->kv_shared != 0 && d->kv_shared != 1) return PA_ERR_INVALID_ARG;
   if (d->kv_format != PA_KV_SAME && d->kv_format != PA_KV_FP8_E4M3) return PA_ERR_INVALID_ARG;
   if (d->waves_per_group != 0 && d->waves_per_group != 1 && d->waves_per_group != 2 &&
-      d->waves_per_group != 4)
+      d->waves_per_group != 4 && d->waves_per_group != 8 && d->waves_per_group != 12)
     return PA_ERR_INVALID_ARG;
   if (d->num_seqs < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
       d->num_q_heads % d->num_kv_heads != 0 || d->max_blocks_per_seq < 1 || d->num_blocks < 1 ||
@@ -1348,12 +1384,10 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
     return PA_ERR_INVALID_ARG;
   }
   if (d->kv_format == PA_KV_FP8_E4M3 && d->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
-  const int waves = d->waves_per_group ? d->waves_per_group : 4;
   const int64_t pairs = int64_t(d->num_seqs) * d->num_kv_heads;
   const int64_t out_rows = int64_t(d->num_seqs) * q_len * d->num_q_heads;
   if (out_rows > INT32_MAX) return PA_ERR_UNSUPPORTED;
   pl->path = path;
-  pl->waves = waves;
   pl->nt = rows > 16 ? 2 : 1;
   pl->rows = int(rows);
   pl->stream = d->kv_shared == 0;
@@ -1361,11 +1395,19 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   pl->tree = false;  // set by the tree entry point
   const bool balanced = path == PA_PATH_MFMA && d->partition_tokens == 0 &&
                         d->num_seqs <= kMaxBalancedSeqs;
+  pl->sched = balanced ? PA_SCHED_BALANCED : PA_SCHED_PARTITIONS;
+  const int max_waves = balanced ? balanced_waves(pl->nt) : 4;
+  if (d->waves_per_group > max_waves) return PA_ERR_UNSUPPORTED;
+  pl->waves = d->waves_per_group ? d->waves_per_group : default_waves(*pl, d->max_context);
+  while (lds_bytes(*pl, d->head_dim, d->num_seqs) > kMaxLdsBytes) {
+    if (d->waves_per_group || pl->waves == 1) return PA_ERR_UNSUPPORTED;
+    pl->waves = pl->waves > 4 ? 4 : pl->waves / 2;
+  }
+  const int waves = pl->waves;
   if (balanced) {
     // grid = resident capacity; the workspace is sized for the largest one
     // (every compute unit full of single-workgroup waves)
-    const int64_t grid_max = int64_t(kCUs) * (32 / waves);
-    pl->sched = PA_SCHED_BALANCED;
+    const int64_t grid_max = int64_t(kCUs) * std::max(1, 32 / waves);
     pl->part_tokens = 0;
     pl->parts = 0;
     pl->grid = int(grid_max);
@@ -1392,7 +1434,6 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   if (parts > kMaxPartitions) return PA_ERR_UNSUPPORTED;
   const int64_t grid = pairs * parts;
   if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
-  pl->sched = PA_SCHED_PARTITIONS;
   pl->part_tokens = pt;
   pl->parts = parts;
   pl->grid = int(grid);
@@ -1403,18 +1444,6 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   return PA_OK;
 }
 
-size_t lds_bytes(const Plan& pl, int D, int num_seqs) {
-  if (pl.path == PA_PATH_MFMA) {
-    const size_t park = size_t(pl.waves) * pl.rows * (D + 2) * sizeof(float);
-    if (pl.sched == PA_SCHED_PARTITIONS) return park;
-    // the park area also holds the merge of a segment's pieces
-    const size_t merge = (size_t(kMergeLdsFloats) + size_t(pl.rows) * D) * sizeof(float);
-    return size_t((num_seqs + 1 + 3) & ~3) * sizeof(int32_t) + std::max(park, merge);
-  }
-  const size_t first = size_t(kValuMaxRows) * D + size_t(pl.waves) * kValuMaxRows * 64;
-  const size_t merge = size_t(pl.waves) * kValuMaxRows * (D + 2);
-  return std::max(first, merge) * sizeof(float);
-}
 
 // Workgroups of `kernel` that fit on the device at once (0 if unknown).
 int resident_groups(const void* kernel, int threads, size_t lds) {

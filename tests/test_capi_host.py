@@ -213,6 +213,21 @@ def test_attention_plan_validation():
               max_blocks_per_seq=8, num_blocks=32, dtype=pa.PA_DTYPE_BF16, max_context=128)
     pl = pa.pa_attention_plan(pa.make_desc(**ok), 1)
     assert pl.path == pa.PA_PATH_MFMA and pl.schedule == _lib.PA_SCHED_BALANCED
+    assert pl.waves_per_group == 4 and pl.tiles_per_wave == 1
+    # long contexts: one workgroup per compute unit holding every resident wave (3 per SIMD)
+    long_ctx = {**ok, "max_context": 8192, "max_blocks_per_seq": 512}
+    pl_long = pa.pa_attention_plan(pa.make_desc(**long_ctx), 1)
+    assert pl_long.waves_per_group == 12 and pl_long.tiles_per_wave == 1
+    pl_long = pa.pa_attention_plan(pa.make_desc(**{**long_ctx, "num_q_heads": 40}), 1)
+    assert pl_long.waves_per_group == 4 and pl_long.tiles_per_wave == 2
+    assert pa.pa_attention_plan(pa.make_desc(**{**long_ctx, "num_q_heads": 40, "waves_per_group": 8}),
+                                1).waves_per_group == 8
+    # 8 waves' park area for 32 rows plus 8192 sequences' step sums exceed the LDS
+    big = {**ok, "num_seqs": 8192, "num_q_heads": 64}
+    assert pa.pa_attention_plan(pa.make_desc(**big), 1).waves_per_group == 4
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_attention_plan(pa.make_desc(**{**big, "waves_per_group": 8}), 1)
+    assert e.value.status == _lib.PA_ERR_UNSUPPORTED
     assert pl.workspace_bytes == pa.pa_attention_workspace_size(pa.make_desc(**ok), 1) > 0
     pl = pa.pa_attention_plan(pa.make_desc(**{**ok, "partition_tokens": 64}), 1)
     assert pl.schedule == _lib.PA_SCHED_PARTITIONS and pl.num_partitions == 2
@@ -230,7 +245,9 @@ def test_attention_plan_validation():
         (dict(num_q_heads=80, num_kv_heads=2), 1, _lib.PA_ERR_UNSUPPORTED),   # 40 rows
         (dict(dtype=pa.PA_DTYPE_F32, path=pa.PA_PATH_MFMA), 1, _lib.PA_ERR_UNSUPPORTED),
         (dict(waves_per_group=3), 1, _lib.PA_ERR_INVALID_ARG),
-        (dict(waves_per_group=8), 1, _lib.PA_ERR_INVALID_ARG),
+        (dict(waves_per_group=16), 1, _lib.PA_ERR_INVALID_ARG),
+        (dict(waves_per_group=8, partition_tokens=64), 1, _lib.PA_ERR_UNSUPPORTED),   # partition kernels: <= 4
+        (dict(waves_per_group=12, num_q_heads=40, num_kv_heads=2), 1, _lib.PA_ERR_UNSUPPORTED),  # two tiles: <= 8
         (dict(kv_format=2), 1, _lib.PA_ERR_INVALID_ARG),
         (dict(kv_format=pa.PA_KV_FP8_E4M3, path=pa.PA_PATH_VALU), 1, _lib.PA_ERR_UNSUPPORTED),
         (dict(kv_format=pa.PA_KV_FP8_E4M3, dtype=pa.PA_DTYPE_F32), 1, _lib.PA_ERR_UNSUPPORTED),
