@@ -14,11 +14,13 @@ Contents (each function cites the passage of the pages it follows):
   kvbytes    closed form for KV-cache bytes per token
   fp8        OCP E4M3 codec and the per-(token, KV head) quantiser
   tree       tree-structured verification: ancestor masks, visible positions
+  spec       speculative decoding's accept / resample step (fixed-point draw)
 
 Pins (tests marked ``not gpu``): brute-force scalar loops, torch's fp64
 scaled_dot_product_attention on the never-paged K/V, the literal block tables
 printed on the pages, the closed form's printed values, invariants (placement,
 prefix sharing, one-token context, zero query, causal rows), torch's
-float8_e4m3fn for the codec, parent-pointer walks for the tree masks, and
-planted mistakes that the pins must catch. No function here is "parity unpinned".
+float8_e4m3fn for the codec, parent-pointer walks for the tree masks, the
+identity P(x) = p(x) for the accept / resample step, and planted mistakes
+that the pins must catch. No function here is "parity unpinned".
 """

@@ -2,8 +2,10 @@
 catch each one: a wrong GQA head map, a wrong scale, an off-by-one causal
 bound, K and V swapped, a transposed V slot, a wrong in-block offset, a
 missing softmax normalisation, a merge without the max rescale, a doubled
-byte count, a FIFO free list, two FP8 codec mistakes, and two tree-mask
-mistakes (ancestor sets cut to the parent, draft positions shifted by one)."""
+byte count, a FIFO free list, two FP8 codec mistakes, two tree-mask
+mistakes (ancestor sets cut to the parent, draft positions shifted by one)
+and three in the accept / resample step (resampling from p instead of the
+residual, the acceptance ratio inverted, a non-strict inverse-CDF bound)."""
 import numpy as np
 import pytest
 
@@ -18,7 +20,9 @@ from tests import test_allocator_model as apins
 from tests import test_oracle_fp8 as fpins
 import oracle.fp8 as ofp8
 import oracle.tree as otree
+import oracle.spec as ospec
 from tests import test_oracle_tree as tpins
+from tests import test_oracle_spec as spins
 
 
 def run_pins():
@@ -40,6 +44,9 @@ def run_pins():
             "llama3_70b_decode_fp8", dict(batch=2, len_const=100)),
         "cow": apins.test_four_samples_share_prompt_then_copy_only_the_diverging_block,
         "tree_literal": tpins.test_ancestor_masks_literal,
+        "spec_identity": spins.test_emitted_token_has_the_target_distribution,
+        "spec_draw": spins.test_draw_boundaries_are_exact,
+        "spec_accept": spins.test_acceptance_is_the_float32_comparison,
         "tree_sdpa": lambda: tpins.test_tree_vs_torch_sdpa_with_parent_walk_mask(dict()),
     }
     failed = []
@@ -109,6 +116,25 @@ def _visible_shifted(L, q_len, mask, i):
     return np.where(pos >= ctx, pos - 1, pos)
 
 
+def _accept_inverted(p_x, q_x, u):
+    p_x, q_x, u = np.float32(p_x), np.float32(q_x), np.float32(u)
+    return bool(q_x >= p_x or np.float32(u * p_x) < q_x)
+
+
+def _draw_non_strict(weights, U):
+    ints = ospec.fixed_weights(weights)
+    S = sum(ints)
+    if S == 0:
+        raise ValueError("all weights are zero")
+    T = (int(U) * S) >> ospec.FIXED_SHIFT
+    run = 0
+    for x, v in enumerate(ints):
+        run += v
+        if run >= T:
+            return x
+    return len(ints) - 1
+
+
 class FifoPool(oalloc.BlockPoolModel):
     def alloc(self):
         if not self._stack:
@@ -142,6 +168,10 @@ MUTANTS = {
                                                    lambda c, s: ofp8.e4m3_decode(c) * 1.0),
     "tree_ancestors_parent_only": lambda mp: mp.setattr(otree, "ancestor_masks", _ancestors_parent_only),
     "tree_nodes_shifted": lambda mp: mp.setattr(otree, "visible_positions", _visible_shifted),
+    "spec_resample_from_target": lambda mp: mp.setattr(ospec, "residual",
+                                                       lambda p, q: np.asarray(p, dtype=np.float32)),
+    "spec_ratio_inverted": lambda mp: mp.setattr(ospec, "accept_draft", _accept_inverted),
+    "spec_draw_non_strict": lambda mp: mp.setattr(ospec, "draw", _draw_non_strict),
 }
 
 

@@ -19,3 +19,4 @@ from .gen import (  # noqa: F401
     sequence,
     tree_parents,
 )
+from .spec import SPEC_CONFIGS, SpecConfig, SpecInputs, generate_spec, spec_config  # noqa: F401,E402
