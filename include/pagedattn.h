@@ -311,6 +311,33 @@ pa_status pa_attention_tree(const pa_attn_desc* desc, const void* q, const void*
                             const uint32_t* tree_mask, int32_t mask_stride, float scale,
                             void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Speculative decoding's accept / resample step (Blog #54, interview
+ * question 3; Part 8, "Thuật Toán Chấp Nhận & Từ Chối Phỏng Đoán"): drafted
+ * token x_k is kept with probability min(1, p_k(x_k) / q_k(x_k)); at the
+ * first rejection the later drafts are dropped and one token is drawn from
+ * max(0, p_k - q_k) renormalised; when all K are kept one more token is drawn
+ * from p_{K+1} (Blog #54, section 2.4 example). Per sequence b, all device:
+ *   p             float32 [B][K+1][vocab] target probabilities
+ *   q             float32 [B][K][vocab] draft probabilities (may be NULL if K = 0)
+ *   draft         int32 [B][K] drafted tokens
+ *   u_accept      float32 [B][K] uniforms in [0, 1), one per acceptance test
+ *   u_draw        uint32 [B] uniform 32-bit integers, one per draw
+ *   num_accepted  int32 [B] out: drafts kept (0..K), or -1 when a drafted
+ *                 token lies outside [0, vocab) (tokens then all -1)
+ *   tokens        int32 [B][K+1] out: the kept drafts, then the drawn token,
+ *                 then -1
+ * The test is taken in float32: keep iff p >= q or u * q < p (one rounding).
+ * The draw: weights w = max(0, p - q) (p - q rounded once; p itself for the
+ * extra token, or when every residual weight is below 2^-32) become
+ * integers floor(w * 2^32); with S their sum and T = floor(U * S / 2^32)
+ * the token drawn is the smallest x whose running sum exceeds T (-1 if
+ * S = 0). Bit-exact and independent of summation order. Asynchronous on
+ * `stream`; PA_ERR_INVALID_ARG for bad sizes or missing pointers. */
+pa_status pa_spec_accept(const float* p, const float* q, const int32_t* draft,
+                         const float* u_accept, const uint32_t* u_draw, int32_t num_seqs,
+                         int32_t num_draft, int32_t vocab, int32_t* num_accepted, int32_t* tokens,
+                         void* stream);
+
 /* The hipError_t of this thread's last HIP call that made a pa_* function
  * return PA_ERR_HIP (0 if none yet), and the HIP runtime's name for a
  * hipError_t value. Diagnostics only. */

@@ -206,3 +206,12 @@ def pa_tree_masks(parents: np.ndarray) -> np.ndarray:
     _check(lib.pa_tree_masks(_i32p(parents), parents.size, masks.ctypes.data_as(C.POINTER(C.c_uint32))),
            "pa_tree_masks")
     return masks
+
+
+def pa_spec_accept(p, q, draft, u_accept, u_draw, num_accepted, tokens, stream=None) -> None:
+    """Device tensors: p float32 [B][K+1][V], q float32 [B][K][V], draft int32 [B][K],
+    u_accept float32 [B][K], u_draw int32/uint32 [B] (bits); outputs num_accepted
+    int32 [B], tokens int32 [B][K+1]."""
+    B, K1, V = p.shape
+    _check(lib.pa_spec_accept(_ptr(p), _ptr(q), _ptr(draft), _ptr(u_accept), _ptr(u_draw), B, K1 - 1, V,
+                              _ptr(num_accepted), _ptr(tokens), _stream(stream)), "pa_spec_accept")

@@ -310,3 +310,16 @@ def test_one_hip_runtime_per_process():
     out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "1"
+
+
+def test_spec_accept_rejects_bad_arguments_before_launch():
+    import ctypes as C
+    fake = 256
+    call = lambda *a: _lib.lib.pa_spec_accept(*a)
+    assert call(fake, fake, fake, fake, fake, 0, 5, 100, fake, fake, None) == _lib.PA_ERR_INVALID_ARG
+    assert call(fake, fake, fake, fake, fake, 4, -1, 100, fake, fake, None) == _lib.PA_ERR_INVALID_ARG
+    assert call(fake, fake, fake, fake, fake, 4, 5, 0, fake, fake, None) == _lib.PA_ERR_INVALID_ARG
+    assert call(None, fake, fake, fake, fake, 4, 5, 100, fake, fake, None) == _lib.PA_ERR_INVALID_ARG
+    assert call(fake, None, fake, fake, fake, 4, 5, 100, fake, fake, None) == _lib.PA_ERR_INVALID_ARG
+    assert call(fake, fake, fake, fake, None, 4, 5, 100, fake, fake, None) == _lib.PA_ERR_INVALID_ARG
+    assert call(fake, fake, fake, fake, fake, 4, 5, 100, None, fake, None) == _lib.PA_ERR_INVALID_ARG
