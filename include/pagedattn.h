@@ -332,11 +332,18 @@ pa_status pa_attention_tree(const pa_attn_desc* desc, const void* q, const void*
  * integers floor(w * 2^32); with S their sum and T = floor(U * S / 2^32)
  * the token drawn is the smallest x whose running sum exceeds T (-1 if
  * S = 0). Bit-exact and independent of summation order. Asynchronous on
- * `stream`; PA_ERR_INVALID_ARG for bad sizes or missing pointers. */
+ * `stream`; PA_ERR_INVALID_ARG for bad sizes, missing pointers or a
+ * workspace smaller than pa_spec_accept_workspace_size. */
 pa_status pa_spec_accept(const float* p, const float* q, const int32_t* draft,
                          const float* u_accept, const uint32_t* u_draw, int32_t num_seqs,
                          int32_t num_draft, int32_t vocab, int32_t* num_accepted, int32_t* tokens,
-                         void* stream);
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pa_spec_accept needs (device, caller-owned: per-chunk
+ * weight sums and per-sequence arrival counters). It must be zero-filled
+ * before its first use; every completed call leaves the counters zero again.
+ * Calls sharing a workspace must not run concurrently. 0 for bad sizes. */
+size_t pa_spec_accept_workspace_size(int32_t num_seqs, int32_t vocab);
 
 /* The hipError_t of this thread's last HIP call that made a pa_* function
  * return PA_ERR_HIP (0 if none yet), and the HIP runtime's name for a

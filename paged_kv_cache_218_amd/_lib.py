@@ -56,7 +56,8 @@ SIGNATURES = [
     ("pa_attention", i32, [C.POINTER(AttnDesc), vp, vp, vp, vp, vp, i32, f32, vp, vp, sz, vp]),
     ("pa_attention_tree", i32, [C.POINTER(AttnDesc), vp, vp, vp, vp, vp, i32, vp, i32, f32, vp, vp, sz, vp]),
     ("pa_tree_masks", i32, [pi32, i32, C.POINTER(C.c_uint32)]),
-    ("pa_spec_accept", i32, [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]),
+    ("pa_spec_accept", i32, [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]),
+    ("pa_spec_accept_workspace_size", sz, [i32, i32]),
     ("pa_last_hip_error", i32, []),
     ("pa_hip_error_name", C.c_char_p, [i32]),
 ]

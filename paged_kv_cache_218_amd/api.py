@@ -208,10 +208,17 @@ def pa_tree_masks(parents: np.ndarray) -> np.ndarray:
     return masks
 
 
-def pa_spec_accept(p, q, draft, u_accept, u_draw, num_accepted, tokens, stream=None) -> None:
+def pa_spec_accept_workspace_size(num_seqs: int, vocab: int) -> int:
+    return int(lib.pa_spec_accept_workspace_size(num_seqs, vocab))
+
+
+def pa_spec_accept(p, q, draft, u_accept, u_draw, num_accepted, tokens, workspace, stream=None) -> None:
     """Device tensors: p float32 [B][K+1][V], q float32 [B][K][V], draft int32 [B][K],
     u_accept float32 [B][K], u_draw int32/uint32 [B] (bits); outputs num_accepted
-    int32 [B], tokens int32 [B][K+1]."""
+    int32 [B], tokens int32 [B][K+1]; workspace: zero-filled before first use, at
+    least pa_spec_accept_workspace_size(B, V) bytes."""
     B, K1, V = p.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib.pa_spec_accept(_ptr(p), _ptr(q), _ptr(draft), _ptr(u_accept), _ptr(u_draw), B, K1 - 1, V,
-                              _ptr(num_accepted), _ptr(tokens), _stream(stream)), "pa_spec_accept")
+                              _ptr(num_accepted), _ptr(tokens), _ptr(workspace), ws_bytes, _stream(stream)),
+           "pa_spec_accept")

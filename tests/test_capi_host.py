@@ -315,11 +315,16 @@ def test_one_hip_runtime_per_process():
 def test_spec_accept_rejects_bad_arguments_before_launch():
     import ctypes as C
     fake = 256
+    ws = pa.pa_spec_accept_workspace_size(4, 100)
+    assert ws > 0 and pa.pa_spec_accept_workspace_size(0, 100) == 0
     call = lambda *a: _lib.lib.pa_spec_accept(*a)
-    assert call(fake, fake, fake, fake, fake, 0, 5, 100, fake, fake, None) == _lib.PA_ERR_INVALID_ARG
-    assert call(fake, fake, fake, fake, fake, 4, -1, 100, fake, fake, None) == _lib.PA_ERR_INVALID_ARG
-    assert call(fake, fake, fake, fake, fake, 4, 5, 0, fake, fake, None) == _lib.PA_ERR_INVALID_ARG
-    assert call(None, fake, fake, fake, fake, 4, 5, 100, fake, fake, None) == _lib.PA_ERR_INVALID_ARG
-    assert call(fake, None, fake, fake, fake, 4, 5, 100, fake, fake, None) == _lib.PA_ERR_INVALID_ARG
-    assert call(fake, fake, fake, fake, None, 4, 5, 100, fake, fake, None) == _lib.PA_ERR_INVALID_ARG
-    assert call(fake, fake, fake, fake, fake, 4, 5, 100, None, fake, None) == _lib.PA_ERR_INVALID_ARG
+    for args in [(fake, fake, fake, fake, fake, 0, 5, 100, fake, fake, fake, ws, None),
+                 (fake, fake, fake, fake, fake, 4, -1, 100, fake, fake, fake, ws, None),
+                 (fake, fake, fake, fake, fake, 4, 5, 0, fake, fake, fake, ws, None),
+                 (None, fake, fake, fake, fake, 4, 5, 100, fake, fake, fake, ws, None),
+                 (fake, None, fake, fake, fake, 4, 5, 100, fake, fake, fake, ws, None),
+                 (fake, fake, fake, fake, None, 4, 5, 100, fake, fake, fake, ws, None),
+                 (fake, fake, fake, fake, fake, 4, 5, 100, None, fake, fake, ws, None),
+                 (fake, fake, fake, fake, fake, 4, 5, 100, fake, fake, None, ws, None),
+                 (fake, fake, fake, fake, fake, 4, 5, 100, fake, fake, fake, ws - 1, None)]:
+        assert call(*args) == _lib.PA_ERR_INVALID_ARG, args

@@ -16,10 +16,16 @@ def run_spec(w, q_none=False):
     B, K = w.draft.shape
     n = torch.empty(B, dtype=torch.int32, device="cuda")
     toks = torch.empty(B, K + 1, dtype=torch.int32, device="cuda")
-    pa.pa_spec_accept(d(w.p), None if q_none else d(w.q), d(w.draft), d(w.u_accept),
-                      d(w.u_draw.view(np.int32)), n, toks)
-    torch.cuda.synchronize()
-    return n.cpu().numpy(), toks.cpu().numpy()
+    ws = torch.zeros(pa.pa_spec_accept_workspace_size(B, w.p.shape[2]), dtype=torch.uint8, device="cuda")
+    for rep in range(2):   # the second call checks that the first left its counters at zero
+        pa.pa_spec_accept(d(w.p), None if q_none else d(w.q), d(w.draft), d(w.u_accept),
+                          d(w.u_draw.view(np.int32)), n, toks, ws)
+        torch.cuda.synchronize()
+        if rep == 0:
+            first = (n.cpu().numpy().copy(), toks.cpu().numpy().copy())
+    assert int(ws[:4 * B].count_nonzero()) == 0
+    assert np.array_equal(first[0], n.cpu().numpy()) and np.array_equal(first[1], toks.cpu().numpy())
+    return first
 
 
 def check(w, seqs=None):
