@@ -15,6 +15,7 @@ Contents (each function cites the passage of the pages it follows):
   fp8        OCP E4M3 codec and the per-(token, KV head) quantiser
   tree       tree-structured verification: ancestor masks, visible positions
   spec       speculative decoding's accept / resample step (fixed-point draw)
+  prefix_cache  radix prefix cache over the pool (match, insert, LRU reclaim)
 
 Pins (tests marked ``not gpu``): brute-force scalar loops, torch's fp64
 scaled_dot_product_attention on the never-paged K/V, the literal block tables

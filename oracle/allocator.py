@@ -100,6 +100,10 @@ class BlockPoolModel:
         if self.refcount[blk] == 0:
             self._stack.append(blk)
 
+    def _must_copy(self, blk: int) -> bool:
+        """A write into blk copies it first: it has other readers."""
+        return self.refcount[blk] > 1
+
     # -- appending / overwriting tokens of one sequence --------------------
     def plan_write(self, table: List[int], capacity: int, num_blocks: int,
                    start_pos: int, n_tokens: int) -> Tuple[int, WritePlan]:
@@ -127,7 +131,7 @@ class BlockPoolModel:
                 raise PoolError(ERR_BAD_BLOCK, f"table entry {j} names free block {table[j]}")
         need = max(0, last_block + 1 - num_blocks)
         need += sum(1 for j in range(first_block, min(num_blocks, last_block + 1))
-                    if self.refcount[table[j]] > 1)
+                    if self._must_copy(table[j]))
         if need > self.num_free:
             raise PoolError(ERR_NO_FREE_BLOCK, "pool cannot supply the write")
 
@@ -135,7 +139,7 @@ class BlockPoolModel:
         for j in range(first_block, last_block + 1):
             if j < num_blocks:
                 old = table[j]
-                if self.refcount[old] > 1:
+                if self._must_copy(old):
                     new = self.alloc()
                     copies.append((old, new))
                     self.free(old)

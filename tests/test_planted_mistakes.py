@@ -4,8 +4,10 @@ bound, K and V swapped, a transposed V slot, a wrong in-block offset, a
 missing softmax normalisation, a merge without the max rescale, a doubled
 byte count, a FIFO free list, two FP8 codec mistakes, two tree-mask
 mistakes (ancestor sets cut to the parent, draft positions shifted by one)
-and three in the accept / resample step (resampling from p instead of the
-residual, the acceptance ratio inverted, a non-strict inverse-CDF bound)."""
+three in the accept / resample step (resampling from p instead of the
+residual, the acceptance ratio inverted, a non-strict inverse-CDF bound) and
+two in the prefix cache (evicting blocks that still have cached children,
+writing into a cached block in place)."""
 import numpy as np
 import pytest
 
@@ -21,6 +23,8 @@ from tests import test_oracle_fp8 as fpins
 import oracle.fp8 as ofp8
 import oracle.tree as otree
 import oracle.spec as ospec
+import oracle.prefix_cache as opc
+from tests import test_prefix_cache_model as pcpins
 from tests import test_oracle_tree as tpins
 from tests import test_oracle_spec as spins
 
@@ -47,6 +51,9 @@ def run_pins():
         "spec_identity": spins.test_emitted_token_has_the_target_distribution,
         "spec_draw": spins.test_draw_boundaries_are_exact,
         "spec_accept": spins.test_acceptance_is_the_float32_comparison,
+        "pc_lru": pcpins.test_lru_evicts_oldest_unreferenced_leaf_first,
+        "pc_cow": pcpins.test_write_into_cached_block_copies_it,
+        "pc_stream": lambda: pcpins.test_random_request_stream_invariants_and_longest_match(1),
         "tree_sdpa": lambda: tpins.test_tree_vs_torch_sdpa_with_parent_walk_mask(dict()),
     }
     failed = []
@@ -135,6 +142,15 @@ def _draw_non_strict(weights, U):
     return len(ints) - 1
 
 
+def _evict_any(self):
+    victim = min(self.unref_time, key=lambda b: (self.unref_time[b], b))
+    del self.children[self.parent[victim]][self.key[victim]]
+    for child in list(self.children[victim].values()):
+        self.parent[child] = None                       # orphans re-hung under the root
+    del self.children[victim], self.parent[victim], self.key[victim], self.unref_time[victim]
+    return victim
+
+
 class FifoPool(oalloc.BlockPoolModel):
     def alloc(self):
         if not self._stack:
@@ -172,6 +188,9 @@ MUTANTS = {
                                                        lambda p, q: np.asarray(p, dtype=np.float32)),
     "spec_ratio_inverted": lambda mp: mp.setattr(ospec, "accept_draft", _accept_inverted),
     "spec_draw_non_strict": lambda mp: mp.setattr(ospec, "draw", _draw_non_strict),
+    "pc_evict_non_leaf": lambda mp: mp.setattr(opc.PrefixCachedPool, "_evict_one", _evict_any),
+    "pc_write_in_place": lambda mp: mp.setattr(opc.PrefixCachedPool, "_must_copy",
+                                               lambda self, blk: self.refcount[blk] > 1),
 }
 
 
