@@ -18,7 +18,11 @@ Readings taken (the pages give the policy, not the mechanics):
   * allocation takes the free list first; when it is empty, the unreferenced
     leaf with the oldest stamp is evicted from the tree and handed out. Only
     leaves are evicted, so every cached block stays reachable through its
-    parent; an unreferenced parent becomes a leaf when its last child goes;
+    parent; an unreferenced parent becomes a leaf when its last child goes.
+    A block is reclaimable when it and its whole subtree are unreferenced
+    (a request may hold a cached block without its parent: insertion follows
+    an existing node with the same tokens, and a write copies a cached block
+    out of a request's table);
   * matching forks each matched block (0 -> 1 revives an unreferenced one)
     and writes it into the request's table; at most the table's capacity;
   * insertion walks the request's full blocks: an existing child with the
@@ -54,9 +58,28 @@ class PrefixCachedPool(BlockPoolModel):
 
     @property
     def num_free(self) -> int:
-        """Blocks an allocation can obtain: the free list plus every
-        unreferenced cached block (each becomes an evictable leaf in turn)."""
-        return len(self._stack) + len(self.unref_time)
+        """Blocks an allocation can obtain: the free list plus every cached
+        block whose whole subtree is unreferenced (each becomes an evictable
+        leaf in turn; a block with a referenced descendant never does)."""
+        return len(self._stack) + self.reclaimable()
+
+    def reclaimable(self) -> int:
+        count = 0
+        live_below: Dict[int, bool] = {}
+        order, stack = [], [None]
+        while stack:                                   # preorder, then children before parents
+            node = stack.pop()
+            order.append(node)
+            stack.extend(self.children[node].values())
+        for node in reversed(order):
+            live = any(live_below[c] for c in self.children[node].values())
+            if node is not None:
+                if self.refcount[node] > 0:
+                    live = True
+                elif not live:
+                    count += 1
+                live_below[node] = live
+        return count
 
     def _must_copy(self, blk: int) -> bool:
         return self.refcount[blk] > 1 or self.cached(blk)
@@ -72,7 +95,7 @@ class PrefixCachedPool(BlockPoolModel):
     def alloc(self) -> int:
         if self._stack:
             return super().alloc()
-        if not self.unref_time:
+        if not any(not self.children[b] for b in self.unref_time):
             raise PoolError(ERR_NO_FREE_BLOCK, "pool exhausted")
         blk = self._evict_one()
         self.refcount[blk] = 1
@@ -137,7 +160,7 @@ class PrefixCachedPool(BlockPoolModel):
 
     def evict(self, max_blocks: int) -> List[int]:
         out = []
-        while len(out) < max_blocks and self.unref_time:
+        while len(out) < max_blocks and any(not self.children[b] for b in self.unref_time):
             blk = self._evict_one()
             self._stack.append(blk)
             out.append(blk)

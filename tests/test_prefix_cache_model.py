@@ -1,6 +1,8 @@
 """Pins of the radix prefix cache model (CPU only): the pages' narrative
 (Part 8, "RadixAttention"), and invariants checked by brute force after
 every operation of random request streams."""
+import copy
+
 import numpy as np
 import pytest
 
@@ -97,6 +99,18 @@ def check_invariants(pool, tables):
     assert set(free) == {b for b in range(nb) if pool.refcount[b] == 0} - cached
     for b, par, _ in pool.dump():
         assert par == -1 or par in cached       # every cached block is reachable from the root
+    # reclaimable: unreferenced blocks with no referenced descendant, by brute force
+    desc = {b: set() for b in cached}
+    for b in cached:
+        x = pool.parent[b]
+        while x is not None:
+            desc[x].add(b)
+            x = pool.parent[x]
+    want = sum(1 for b in unref if all(pool.refcount[d] == 0 for d in desc[b]))
+    assert pool.reclaimable() == want
+    # draining the cache hands out exactly that many blocks
+    probe = copy.deepcopy(pool)
+    assert len(probe.evict(10 ** 6)) == want
 
 
 @pytest.mark.parametrize("seed", range(4))
