@@ -105,6 +105,7 @@ const char* pa_status_string(pa_status s);
 /* ------------------------------------------------------------------------ */
 
 typedef struct pa_pool pa_pool;
+typedef struct pa_prefix_cache pa_prefix_cache;
 
 /* Create the host-side bookkeeping of a pool of num_blocks physical blocks:
  * a reference count per block (all 0) and a LIFO free list. The free list's
@@ -310,6 +311,64 @@ pa_status pa_attention_tree(const pa_attn_desc* desc, const void* q, const void*
                             const int32_t* context_lens, int32_t q_len,
                             const uint32_t* tree_mask, int32_t mask_stride, float scale,
                             void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Radix prefix cache (Part 8, "RadixAttention"; "Mở rộng Quy mô và
+ * Triển khai", "Cache Tiền tố") -------------------------------------------
+ * Host bookkeeping attached to a pool: the KV blocks of earlier requests are
+ * kept in a prefix tree, a request whose tokens match a cached prefix reuses
+ * those physical blocks (reference count + 1, no prefill for them), and under
+ * memory pressure unreferenced cached blocks are reclaimed least recently
+ * used first. Mechanics (this library's reading):
+ *   - one tree node per full block, keyed by its block_size token ids;
+ *   - a cached block whose count falls to 0 stays in the tree, unreferenced,
+ *     stamped by a counter bumped at each such event; it is not on the free
+ *     list (pa_pool_num_free does not count it);
+ *   - pa_block_alloc and pa_write_kv take the free list first, then evict the
+ *     unreferenced leaf with the oldest stamp; a block is reclaimable when it
+ *     and its whole subtree are unreferenced, and availability checks count
+ *     those (so a write either fits or changes nothing);
+ *   - a write into a cached block copies it first, even at count 1.
+ * Tokens are host int32 ids; tables are host int32 block ids. */
+
+/* Attach a prefix cache to `pool` (one per pool; PA_ERR_INVALID_ARG if it
+ * already has one). pa_pool_destroy also destroys an attached cache. */
+pa_status pa_prefix_cache_create(pa_pool* pool, pa_prefix_cache** out);
+
+/* Detach and delete: reclaimable blocks go to the free list in eviction
+ * order, then every other unreferenced cached block in stamp order; blocks
+ * still referenced return to the free list when released. */
+void pa_prefix_cache_destroy(pa_prefix_cache* cache);
+
+/* Longest cached prefix of whole blocks of tokens[0..n_tokens), at most
+ * `capacity` blocks: writes them to table[0..*n_blocks) and forks each
+ * (an unreferenced one is referenced again). The caller continues writing at
+ * position *n_blocks * block_size. */
+pa_status pa_prefix_match(pa_prefix_cache* cache, const int32_t* tokens, int32_t n_tokens,
+                          int32_t* table, int32_t capacity, int32_t* n_blocks);
+
+/* Cache a request's full blocks: tokens[0..n_tokens) held in table[0..n_blocks)
+ * (only final tokens: a cached block is never written again). Walking the
+ * tree, an existing node with the same tokens is followed; otherwise the
+ * request's block becomes that node. *n_new (nullable) = nodes added.
+ * PA_ERR_INVALID_ARG if a block to add is out of range or already cached
+ * under another prefix, PA_ERR_BAD_BLOCK if it is free; nothing changes then. */
+pa_status pa_prefix_insert(pa_prefix_cache* cache, const int32_t* tokens, int32_t n_tokens,
+                           const int32_t* table, int32_t n_blocks, int32_t* n_new);
+
+/* Evict up to max_blocks reclaimable blocks (LRU leaves first) onto the free
+ * list's head; their ids in eviction order go to `evicted` (nullable). */
+pa_status pa_prefix_evict(pa_prefix_cache* cache, int32_t max_blocks, int32_t* evicted,
+                          int32_t* n_evicted);
+
+/* Counts of cached, unreferenced cached, and reclaimable blocks (nullable). */
+pa_status pa_prefix_cache_stats(const pa_prefix_cache* cache, int32_t* cached,
+                                int32_t* unreferenced, int32_t* reclaimable);
+
+/* Every cached block in ascending id order with its parent block (-1: child
+ * of the root) and unreferenced stamp (-1: referenced). *n = the count;
+ * PA_ERR_INVALID_ARG if capacity is smaller (only *n is written then). */
+pa_status pa_prefix_cache_dump(const pa_prefix_cache* cache, int32_t* blocks, int32_t* parents,
+                               int64_t* stamps, int32_t capacity, int32_t* n);
 
 /* Speculative decoding's accept / resample step (Blog #54, interview
  * question 3; Part 8, "Thuật Toán Chấp Nhận & Từ Chối Phỏng Đoán"): drafted

@@ -58,6 +58,13 @@ SIGNATURES = [
     ("pa_tree_masks", i32, [pi32, i32, C.POINTER(C.c_uint32)]),
     ("pa_spec_accept", i32, [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]),
     ("pa_spec_accept_workspace_size", sz, [i32, i32]),
+    ("pa_prefix_cache_create", i32, [vp, C.POINTER(vp)]),
+    ("pa_prefix_cache_destroy", None, [vp]),
+    ("pa_prefix_match", i32, [vp, pi32, i32, pi32, i32, pi32]),
+    ("pa_prefix_insert", i32, [vp, pi32, i32, pi32, i32, pi32]),
+    ("pa_prefix_evict", i32, [vp, i32, pi32, pi32]),
+    ("pa_prefix_cache_stats", i32, [vp, pi32, pi32, pi32]),
+    ("pa_prefix_cache_dump", i32, [vp, pi32, pi32, C.POINTER(i64), i32, pi32]),
     ("pa_last_hip_error", i32, []),
     ("pa_hip_error_name", C.c_char_p, [i32]),
 ]

@@ -72,6 +72,19 @@ class Pool:
             self.handle = None
 
 
+class PrefixCache:
+    """Owned pa_prefix_cache handle; keeps its pool alive."""
+
+    def __init__(self, handle: int, pool: "Pool"):
+        self.handle = handle
+        self.pool = pool
+
+    def __del__(self):
+        if getattr(self, "handle", None) and getattr(self.pool, "handle", None):
+            lib.pa_prefix_cache_destroy(self.handle)
+            self.handle = None
+
+
 def pa_status_string(status: int) -> str:
     return lib.pa_status_string(status).decode()
 
@@ -222,3 +235,64 @@ def pa_spec_accept(p, q, draft, u_accept, u_draw, num_accepted, tokens, workspac
     _check(lib.pa_spec_accept(_ptr(p), _ptr(q), _ptr(draft), _ptr(u_accept), _ptr(u_draw), B, K1 - 1, V,
                               _ptr(num_accepted), _ptr(tokens), _ptr(workspace), ws_bytes, _stream(stream)),
            "pa_spec_accept")
+
+
+# -- radix prefix cache -------------------------------------------------------
+
+def pa_prefix_cache_create(pool: Pool) -> PrefixCache:
+    h = C.c_void_p()
+    _check(lib.pa_prefix_cache_create(pool.handle, C.byref(h)), "pa_prefix_cache_create")
+    return PrefixCache(h.value, pool)
+
+
+def pa_prefix_cache_destroy(cache: PrefixCache) -> None:
+    if cache.handle:
+        lib.pa_prefix_cache_destroy(cache.handle)
+        cache.handle = None
+
+
+def _tokens(tokens) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+
+
+def pa_prefix_match(cache: PrefixCache, tokens, table: np.ndarray) -> int:
+    """Fills table[0..n) with the longest cached prefix (at most table.size blocks); returns n."""
+    t = _tokens(tokens)
+    n = C.c_int32()
+    _check(lib.pa_prefix_match(cache.handle, _i32p(t), t.size, _i32p(table), table.size, C.byref(n)),
+           "pa_prefix_match")
+    return n.value
+
+
+def pa_prefix_insert(cache: PrefixCache, tokens, table: np.ndarray, num_blocks: int) -> int:
+    t = _tokens(tokens)
+    n = C.c_int32()
+    _check(lib.pa_prefix_insert(cache.handle, _i32p(t), t.size, _i32p(table), num_blocks, C.byref(n)),
+           "pa_prefix_insert")
+    return n.value
+
+
+def pa_prefix_evict(cache: PrefixCache, max_blocks: int) -> list:
+    out = np.zeros(max(max_blocks, 1), dtype=np.int32)
+    n = C.c_int32()
+    _check(lib.pa_prefix_evict(cache.handle, max_blocks, _i32p(out), C.byref(n)), "pa_prefix_evict")
+    return out[:n.value].tolist()
+
+
+def pa_prefix_cache_stats(cache: PrefixCache):
+    a, b, c = C.c_int32(), C.c_int32(), C.c_int32()
+    _check(lib.pa_prefix_cache_stats(cache.handle, C.byref(a), C.byref(b), C.byref(c)), "pa_prefix_cache_stats")
+    return a.value, b.value, c.value
+
+
+def pa_prefix_cache_dump(cache: PrefixCache) -> list:
+    """[(block, parent or -1, unreferenced stamp or -1)] in ascending block order."""
+    n = C.c_int32()
+    lib.pa_prefix_cache_dump(cache.handle, None, None, None, 0, C.byref(n))
+    k = n.value
+    blocks, parents = np.zeros(max(k, 1), np.int32), np.zeros(max(k, 1), np.int32)
+    stamps = np.zeros(max(k, 1), np.int64)
+    _check(lib.pa_prefix_cache_dump(cache.handle, _i32p(blocks), _i32p(parents),
+                                    stamps.ctypes.data_as(C.POINTER(C.c_int64)), k, C.byref(n)),
+           "pa_prefix_cache_dump")
+    return [(int(blocks[i]), int(parents[i]), int(stamps[i])) for i in range(k)]

@@ -22,7 +22,7 @@ HIPCC = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["attention.hip", "kvwrite.hip", "spec.hip"]
-HOST_SOURCES = ["pool.cpp"]
+HOST_SOURCES = ["pool.cpp", "prefix_cache.cpp"]
 HIP_FLAGS = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]

@@ -15,6 +15,7 @@ struct pa_pool {
   int32_t dtype = 0;
   std::vector<int32_t> refcount;  // per physical block
   std::vector<int32_t> stack;     // free list; back() is the head
+  pa_prefix_cache* cache = nullptr;  // attached prefix cache, if any
 };
 
 namespace pa {
@@ -28,6 +29,13 @@ inline int32_t elem_bytes(int32_t dtype) {
 inline int64_t fp8_codes_bytes(int64_t num_blocks, int64_t hkv, int64_t bs, int64_t d) {
   return num_blocks * hkv * bs * d;
 }
+
+// Prefix-cache hooks used by the pool (defined with the cache).
+bool cache_holds(const pa_pool* p, int32_t block);       // block is in the tree
+void cache_unreferenced(pa_pool* p, int32_t block);      // a cached block's count fell to 0
+int64_t cache_reclaimable(const pa_pool* p);             // blocks eviction can still free
+int32_t cache_evict_one(pa_pool* p);                     // LRU unreferenced leaf, or -1
+void cache_release(pa_prefix_cache* c);                  // detach from the pool and delete
 
 // Record a failed HIP call (this thread's last one, read by pa_last_hip_error)
 // and return PA_ERR_HIP. Defined with the HIP sources.

@@ -82,28 +82,55 @@ extern "C" pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, int3
   return PA_OK;
 }
 
-extern "C" void pa_pool_destroy(pa_pool* pool) { delete pool; }
+extern "C" void pa_pool_destroy(pa_pool* pool) {
+  if (!pool) return;
+  if (pool->cache) pa::cache_release(pool->cache);
+  delete pool;
+}
 
 namespace {
 
 bool in_range(const pa_pool* p, int32_t b) { return b >= 0 && b < p->num_blocks; }
 
+// Whether `need` blocks can be handed out: the free list, then (with a prefix
+// cache) the cached blocks eviction can still free.
+bool can_supply(const pa_pool* p, int64_t need) {
+  int64_t avail = int64_t(p->stack.size());
+  if (need > avail && p->cache) avail += pa::cache_reclaimable(p);
+  return need <= avail;
+}
+
+// Callers check can_supply first.
 int32_t pop_free(pa_pool* p) {
-  int32_t b = p->stack.back();
-  p->stack.pop_back();
+  int32_t b;
+  if (!p->stack.empty()) {
+    b = p->stack.back();
+    p->stack.pop_back();
+  } else {
+    b = pa::cache_evict_one(p);
+  }
   p->refcount[b] = 1;
   return b;
 }
 
 void release(pa_pool* p, int32_t b) {
-  if (--p->refcount[b] == 0) p->stack.push_back(b);
+  if (--p->refcount[b] == 0) {
+    if (p->cache && pa::cache_holds(p, b)) pa::cache_unreferenced(p, b);  // stays cached
+    else p->stack.push_back(b);
+  }
+}
+
+// A write into block b copies it first: other sequences read it, or the
+// prefix cache keeps its contents.
+bool must_copy(const pa_pool* p, int32_t b) {
+  return p->refcount[b] > 1 || (p->cache && pa::cache_holds(p, b));
 }
 
 }  // namespace
 
 extern "C" pa_status pa_block_alloc(pa_pool* pool, int32_t* block_id) {
   if (!pool || !block_id) return PA_ERR_INVALID_ARG;
-  if (pool->stack.empty()) return PA_ERR_NO_FREE_BLOCK;
+  if (!can_supply(pool, 1)) return PA_ERR_NO_FREE_BLOCK;
   *block_id = pop_free(pool);
   return PA_OK;
 }
@@ -170,16 +197,16 @@ pa_status plan_write(pa_pool* p, int32_t* table, int32_t capacity, int32_t* live
     const int32_t b = table[j];
     if (!in_range(p, b)) return PA_ERR_INVALID_ARG;
     if (p->refcount[b] == 0) return PA_ERR_BAD_BLOCK;
-    if (p->refcount[b] > 1) ++n_copy;
+    if (must_copy(p, b)) ++n_copy;
   }
   need += n_copy;
   if (copies && n_copy > max_copies) return PA_ERR_INVALID_ARG;
-  if (need > int64_t(p->stack.size())) return PA_ERR_NO_FREE_BLOCK;
+  if (!can_supply(p, need)) return PA_ERR_NO_FREE_BLOCK;
 
   for (int32_t j = first_block; j <= last; ++j) {
     if (j < live) {
       const int32_t old = table[j];
-      if (p->refcount[old] > 1) {
+      if (must_copy(p, old)) {
         const int32_t fresh = pop_free(p);
         if (copies) {
           copies->push_back(old);

@@ -23,6 +23,80 @@
     }                                                                   \
   } while (0)
 
+// Requests sharing a few prompts against a pool with a prefix cache: match,
+// write, insert, rewrite, finish and evict at random; the sum of the tables'
+// holdings must equal the refcounts, and free + cached + held must cover the
+// pool. Destroying the pool with the cache attached must free everything.
+static void prefix_cache_stress() {
+  const int NB = 96, BS = 16, CAP = 10, NSEQ = 12;
+  std::mt19937 rng(7);
+  pa_pool* pool = nullptr;
+  CHECK(pa_pool_create(NB, BS, 2, 64, PA_DTYPE_BF16, nullptr, &pool) == PA_OK);
+  pa_prefix_cache* cache = nullptr;
+  CHECK(pa_prefix_cache_create(pool, &cache) == PA_OK);
+  std::vector<std::vector<int32_t>> prompts(4);
+  for (auto& pr : prompts) {
+    pr.resize(BS * (1 + rng() % 5) + rng() % BS);
+    for (auto& t : pr) t = int32_t(rng() % 3);
+  }
+  std::vector<std::vector<int32_t>> tables(NSEQ, std::vector<int32_t>(CAP, -1)), toks(NSEQ);
+  std::vector<int32_t> live(NSEQ, 0);
+  for (int step = 0; step < 20000; ++step) {
+    const int s = int(rng() % NSEQ), op = int(rng() % 6);
+    if (live[s] == 0) {  // start a request
+      toks[s] = prompts[rng() % prompts.size()];
+      for (int k = int(rng() % BS); k > 0; --k) toks[s].push_back(int32_t(rng() % 3));
+      if (int(toks[s].size()) > CAP * BS) toks[s].resize(CAP * BS);
+      int32_t n = 0;
+      CHECK(pa_prefix_match(cache, toks[s].data(), int32_t(toks[s].size()), tables[s].data(), CAP, &n) == PA_OK);
+      int32_t lv = n;
+      const pa_status st = pa_write_plan(pool, tables[s].data(), CAP, &lv, n * BS,
+                                         int32_t(toks[s].size()) - n * BS, nullptr, 0, nullptr, nullptr);
+      if (st == PA_OK) {
+        live[s] = lv;
+      } else {
+        CHECK(st == PA_ERR_NO_FREE_BLOCK);
+        for (int j = 0; j < n; ++j) CHECK(pa_block_free(pool, tables[s][j]) == PA_OK);
+        tables[s].assign(CAP, -1);
+      }
+    } else if (op == 0) {
+      int32_t added = 0;
+      const pa_status st = pa_prefix_insert(cache, toks[s].data(), int32_t(toks[s].size()), tables[s].data(),
+                                            live[s], &added);
+      CHECK(st == PA_OK || st == PA_ERR_INVALID_ARG);
+    } else if (op == 1) {  // rewrite one position
+      int32_t lv = live[s];
+      const int32_t pos = int32_t(rng() % (live[s] * BS));
+      const pa_status st = pa_write_plan(pool, tables[s].data(), CAP, &lv, pos, 1, nullptr, 0, nullptr, nullptr);
+      CHECK(st == PA_OK || st == PA_ERR_NO_FREE_BLOCK);
+    } else if (op == 2) {
+      int32_t ev[8], n = 0;
+      CHECK(pa_prefix_evict(cache, int32_t(rng() % 8), ev, &n) == PA_OK);
+    } else {  // finish
+      for (int j = 0; j < live[s]; ++j) CHECK(pa_block_free(pool, tables[s][j]) == PA_OK);
+      tables[s].assign(CAP, -1);
+      live[s] = 0;
+    }
+    if (step % 53 == 0) {
+      std::vector<int32_t> held(NB, 0);
+      for (int q = 0; q < NSEQ; ++q)
+        for (int j = 0; j < live[q]; ++j) ++held[tables[q][j]];
+      int32_t nfree = 0, cached = 0, unref = 0, recl = 0;
+      CHECK(pa_pool_num_free(pool, &nfree) == PA_OK);
+      CHECK(pa_prefix_cache_stats(cache, &cached, &unref, &recl) == PA_OK);
+      int referenced = 0;
+      for (int b = 0; b < NB; ++b) {
+        int32_t rc = -1;
+        CHECK(pa_block_refcount(pool, b, &rc) == PA_OK);
+        CHECK(rc == held[b]);
+        referenced += rc > 0;
+      }
+      CHECK(nfree + unref + referenced == NB && recl <= unref);
+    }
+  }
+  pa_pool_destroy(pool);  // also destroys the attached cache
+}
+
 int main() {
   const int NB = 96, BS = 16, CAP = 24, NSEQ = 8;
   std::mt19937 rng(218);
@@ -125,6 +199,7 @@ int main() {
     check_invariants();
   }
   pa_pool_destroy(pool);
+  prefix_cache_stress();
   std::printf("pool stress ok\n");
   return 0;
 }
