@@ -66,6 +66,24 @@ class PagedKVCache:
         self.live[b] = api.pa_write_kv(self.pool, self.k_pool, self.v_pool, row, self.live[b],
                                        start_pos, k_new, v_new, stream)
 
+    # -- radix prefix cache ------------------------------------------------
+    def enable_prefix_cache(self):
+        self.prefix = api.pa_prefix_cache_create(self.pool)
+        return self.prefix
+
+    def match_prefix(self, b: int, tokens) -> int:
+        """Sequence b (empty) starts with the longest cached prefix of tokens;
+        returns the number of tokens it covers (write from there on)."""
+        assert self.live[b] == 0
+        n = api.pa_prefix_match(self.prefix, tokens, self.tables[b])
+        self.live[b] = n
+        self.shared = self.shared or n > 0
+        return n * self.bs
+
+    def insert_prefix(self, b: int, tokens) -> int:
+        """Cache sequence b's full blocks of tokens (their K/V already written)."""
+        return api.pa_prefix_insert(self.prefix, tokens, self.tables[b], self.live[b])
+
     def share_blocks(self, src: int, dst: int, n_blocks: int) -> None:
         """Sequence dst starts with the first n_blocks blocks of src (forked)."""
         for j in range(n_blocks):
