@@ -135,7 +135,8 @@ def _pmc_rows(run_dir):
     return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(open(path))]
 
 
-def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_bytes: int = 2**30):
+def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_bytes: int = 2**30,
+                bench_json: str = None):
     """Turn two rocprofv3 --pmc runs of `bench.py --copy-probe` (FETCH_SIZE,
     then WRITE_SIZE; KiB per dispatch) into HBM bytes per launch of the main
     kernel. Each counter is scaled by copy_bytes over what it reads for the
@@ -143,6 +144,12 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_bytes: int =
     import statistics
     import workloads
     import paged_kv_cache_218_amd as pa
+    if workload in workloads.SPEC_CONFIGS:
+        # data-dependent bytes: taken from the bench line of the same workload
+        rec = json.loads(open(bench_json).read().strip().splitlines()[-1])
+        out = {"workload": workload, "kernel": rec["roofline"]["kernel"], "source_sha256": source_digest(),
+               "algorithmic_bytes": rec["algorithmic_bytes"]}
+        return _pmc_finish(out, fetch_dir, write_dir, copy_bytes, out["kernel"], workload)
     cfg = workloads.CONFIGS[workload]
     lens = workloads.context_lengths(cfg)
     nb = workloads.pool_blocks(cfg, lens)
@@ -155,6 +162,11 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_bytes: int =
     kernel = kernel_name(cfg, plan, desc)
     out = {"workload": workload, "kernel": kernel, "source_sha256": source_digest(),
            "algorithmic_bytes": algorithmic_bytes(cfg, lens)}
+    return _pmc_finish(out, fetch_dir, write_dir, copy_bytes, kernel, workload)
+
+
+def _pmc_finish(out, fetch_dir, write_dir, copy_bytes, kernel, workload):
+    import statistics
     for name, d in (("fetch", fetch_dir), ("write", write_dir)):
         rows = _pmc_rows(d)
         copy = [v for k, v in rows if "copyBuffer" in k and v * 1024 > 0.25 * copy_bytes]
@@ -263,6 +275,8 @@ def bench_spec(args):
                      "note": "one kernel per step: launch time from HIP events over the timed region"},
         "wall_s_timed_region": round(t_wall, 4),
     }
+    if args.copy_probe:
+        result["copy_probe"] = copy_probe()
     if not args.no_cpu_baseline:
         from oracle import spec as ospec
         t0 = time.perf_counter()
@@ -292,9 +306,10 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--bench-json", help="with --pmc-summary: a bench line of the workload (data-dependent bytes)")
     args = ap.parse_args()
     if args.pmc_summary:
-        pmc_summary(args.workload, *args.pmc_summary)
+        pmc_summary(args.workload, *args.pmc_summary, bench_json=args.bench_json)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
