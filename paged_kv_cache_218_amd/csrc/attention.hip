@@ -744,107 +744,56 @@ __device__ __forceinline__ int64_t owner(int64_t x, int64_t S, int64_t N) {
   return k;
 }
 
-// LDS floats the merge of a segment's pieces needs beyond the R x D output
-// accumulators (it reuses the park area): per-row partial maxima and sums of
-// up to 8 thread groups, the rows' final ones and a chunk of piece weights.
-constexpr int kMergeChunk = 64;  // pieces whose weights sit in LDS at once
-constexpr int kMergeLdsFloats = 2 * 8 * 32 + 2 * 32 + kMergeChunk * 32;
-constexpr int kMergeBatch = 8;   // partial loads in flight per thread
+constexpr int kMergeBatch = 8;   // pieces whose partial loads a thread has in flight at once
 #ifndef PA_MIN_GROUP_STEPS
 #define PA_MIN_GROUP_STEPS 8
 #endif
 constexpr int kMinGroupSteps = PA_MIN_GROUP_STEPS;  // fewest steps a workgroup's range holds
 
 // The workgroup that completed a segment merges its npieces partials, which
-// start at piece p0 (log-sum-exp identity: M = max m_p, w_p = l_p 2^(m_p - M),
-// out = sum_p w_p o_p / sum_p w_p). The (m, l) pairs are folded by thread
-// groups into online (max, sum) per row; the weighted sums of o run over
-// 4-column chunks with kMergeBatch independent loads in flight. out0: the
-// segment's first output row.
+// start at piece p0 (log-sum-exp identity: out = sum_p w_p o_p / sum_p w_p
+// with w_p = l_p 2^(m_p - M), M = max_p m_p). Each thread owns 4-column
+// chunks of the output rows and folds the pieces into a running (max, sum,
+// weighted o) in piece order; the (m, l) and o loads of kMergeBatch pieces
+// are issued together, so a merge of up to kMergeBatch pieces costs one
+// round trip to memory. out0: the segment's first output row.
 template <int D>
-__device__ void merge_pieces(const AttnArgs& a, int64_t p0, int npieces, int R, uint16_t* out0,
-                             float* lds) {
+__device__ void merge_pieces(const AttnArgs& a, int64_t p0, int npieces, int R, uint16_t* out0) {
   // The opaque copy keeps the thread-index arithmetic below inside this
   // function: hoisted out of the caller's loop it would stay live across
   // the attention steps and cost registers there.
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int T = blockDim.x;
-  const int QN = min(8, T / 32);   // thread groups per row for the row statistics
-  float* red_m = lds;              // [8][32]
-  float* red_l = red_m + 8 * 32;   // [8][32]
-  float* row_M = red_l + 8 * 32;   // [32]
-  float* row_den = row_M + 32;     // [32]
-  float* wts = row_den + 32;       // [kMergeChunk][32]
-  f32x4* acc_s = reinterpret_cast<f32x4*>(wts + kMergeChunk * 32);  // [R * D / 4]
   const auto ml_r = partial_rsrc(a.part_ml + p0 * R * 2, uint32_t(npieces) * R * 8);
   const auto o_r = partial_rsrc(a.part_o + p0 * R * D, uint32_t(npieces) * R * D * 4);
   const int nc = R * D / 4;
-  for (int e = tid; e < nc; e += T) acc_s[e] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  // row statistics: thread (q, r) folds pieces q, q + QN, ... of row r
-  {
-    const int r = tid % 32, q = tid / 32;
-    float m_run = -INFINITY, l_run = 0.f;
-    if (r < R && q < QN) {
-      for (int p = q; p < npieces; p += 4 * QN) {
-        f32x2 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = load2_coherent(ml_r, uint32_t((p + QN * u) * R + r) * 8);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (p + QN * u < npieces) {
-            const float m_new = fmaxf(m_run, v[u][0]);
-            const float mu = m_new == -INFINITY ? 0.f : m_new;
-            l_run = l_run * fast_exp2(m_run - mu) + v[u][1] * fast_exp2(v[u][0] - mu);
-            m_run = m_new;
-          }
-        }
-      }
-      red_m[q * 32 + r] = m_run;
-      red_l[q * 32 + r] = l_run;
-    }
-    __syncthreads();
-    if (tid < R) {
-      float M = -INFINITY;
-      for (int qq = 0; qq < QN; ++qq) M = fmaxf(M, red_m[qq * 32 + tid]);
-      const float mu = M == -INFINITY ? 0.f : M;
-      float den = 0.f;
-      for (int qq = 0; qq < QN; ++qq) den += red_l[qq * 32 + tid] * fast_exp2(red_m[qq * 32 + tid] - mu);
-      row_M[tid] = mu;
-      row_den[tid] = den;
-    }
-    __syncthreads();
-  }
-  // weighted sums, kMergeChunk pieces at a time (uniform loop: every thread
-  // reaches every barrier)
-  for (int pc = 0; pc < npieces; pc += kMergeChunk) {
-    const int n = min(kMergeChunk, npieces - pc);
-    for (int e = tid; e < n * R; e += T) {
-      const int pp = e / R, rr = e % R;
-      const f32x2 v = load2_coherent(ml_r, uint32_t((pc + pp) * R + rr) * 8);
-      wts[pp * 32 + rr] = v[1] * fast_exp2(v[0] - row_M[rr]);
-    }
-    __syncthreads();
-    for (int ch = tid; ch < nc; ch += T) {
-      const int r = ch / (D / 4), c = 4 * (ch % (D / 4));
-      f32x4 acc = acc_s[ch];
-      for (int p = 0; p < n; p += kMergeBatch) {
-        f32x4 o[kMergeBatch];
-#pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u)
-          o[u] = load4_coherent(o_r, uint32_t(((pc + p + u) * R + r) * D + c) * 4);
-#pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u)
-          if (p + u < n) acc += wts[(p + u) * 32 + r] * o[u];
-      }
-      acc_s[ch] = acc;
-    }
-    __syncthreads();
-  }
   for (int ch = tid; ch < nc; ch += T) {
     const int r = ch / (D / 4), c = 4 * (ch % (D / 4));
-    const float den = row_den[r];
-    const f32x4 acc = acc_s[ch];
+    float M = -INFINITY, den = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int pb = 0; pb < npieces; pb += kMergeBatch) {
+      // loads past the last piece fall outside the buffer range and read 0
+      f32x2 ml[kMergeBatch];
+      f32x4 o[kMergeBatch];
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        ml[u] = load2_coherent(ml_r, uint32_t((pb + u) * R + r) * 8);
+        o[u] = load4_coherent(o_r, uint32_t(((pb + u) * R + r) * D + c) * 4);
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        if (pb + u < npieces) {
+          const float m = ml[u][0], l = ml[u][1];
+          const float m_new = fmaxf(M, m);
+          const float mu = m_new == -INFINITY ? 0.f : m_new;
+          const float f_old = fast_exp2(M - mu), w = l * fast_exp2(m - mu);
+          den = den * f_old + w;
+          acc = acc * f_old + w * o[u];
+          M = m_new;
+        }
+      }
+    }
     const int i = r / a.group, hh = r % a.group;  // drafted token, head within the group
     uint16_t* dst = out0 + (int64_t(i) * a.hq + hh) * D + c;
 #pragma unroll
@@ -996,7 +945,7 @@ __global__ __launch_bounds__(64 * balanced_waves(NT)) void mfma_attn_balanced(At
     const int64_t seg = duty_seg[d];
     const int bb = int(seg / a.hkv), gg = int(seg % a.hkv);
     merge_pieces<D>(a, duty_p0[d], duty_n[d], R,
-                    static_cast<uint16_t*>(a.out) + int64_t(out_row(a, bb, gg, 0)) * D, park);
+                    static_cast<uint16_t*>(a.out) + int64_t(out_row(a, bb, gg, 0)) * D);
     if (threadIdx.x == 0)  // ready for the next call
       __hip_atomic_store(&a.counters[seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
@@ -1327,9 +1276,7 @@ size_t lds_bytes(const Plan& pl, int D, int num_seqs) {
   if (pl.path == PA_PATH_MFMA) {
     const size_t park = size_t(pl.waves) * pl.rows * (D + 2) * sizeof(float);
     if (pl.sched == PA_SCHED_PARTITIONS) return park;
-    // the park area also holds the merge of a segment's pieces
-    const size_t merge = (size_t(kMergeLdsFloats) + size_t(pl.rows) * D) * sizeof(float);
-    return size_t((num_seqs + 1 + 3) & ~3) * sizeof(int32_t) + std::max(park, merge);
+    return size_t((num_seqs + 1 + 3) & ~3) * sizeof(int32_t) + park;  // step prefix sums, then the park area
   }
   const size_t first = size_t(kValuMaxRows) * D + size_t(pl.waves) * kValuMaxRows * 64;
   const size_t merge = size_t(pl.waves) * kValuMaxRows * (D + 2);
