@@ -1,7 +1,7 @@
 """Paged decode attention throughput on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--path auto|mfma|valu]
-                    [--partition-tokens N] [--no-cpu-baseline] [--copy-probe]
+                    [--partition-tokens N] [--no-cpu-baseline] [--copy-probe] [--read-probe]
 
 A step is one pa_attention call (pa_attention_tree for a tree of drafted
 tokens) over the whole batch of the workload (every sequence, every query
@@ -189,6 +189,40 @@ def _pmc_finish(out, fetch_dir, write_dir, copy_bytes, kernel, workload):
     print(json.dumps(out, indent=1))
 
 
+def read_probe(gib: int = 4, reps: int = 10):
+    """Practical HBM read ceiling: the library's read probe over a `gib` GiB
+    buffer read once per call as 8 KiB blocks in a seeded random order (the
+    attention kernels' access pattern), over a few launch shapes; the best
+    rate is the ceiling the attention kernels are compared with."""
+    import torch
+    import paged_kv_cache_218_amd as pa
+    n_blocks = gib * 2**30 // 8192
+    buf = torch.ones(n_blocks * 8192, dtype=torch.uint8, device="cuda")
+    gen = torch.Generator().manual_seed(218)
+    order = torch.randperm(n_blocks, generator=gen).to(torch.int32).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rows = []
+    for depth in (1, 2, 4):
+        for waves_per_cu in (8, 16, 32):
+            wgs = 256 * waves_per_cu // 4
+            for _ in range(2):
+                pa.pa_read_probe(buf, order, depth, wgs, sink)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                pa.pa_read_probe(buf, order, depth, wgs, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / reps * 1e3
+            rows.append({"blocks_in_flight": depth, "workgroups": wgs, "us": round(us, 1),
+                         "gbs": round(n_blocks * 8192 / us / 1e3, 1)})
+            log(f"read probe: {depth} blocks in flight per wave, {wgs} workgroups: {us:.1f} us, {rows[-1]['gbs']} GB/s")
+    best = max(rows, key=lambda r: r["gbs"])
+    return {"bytes": n_blocks * 8192, "order": "seeded random permutation of 8 KiB blocks",
+            "best_gbs": best["gbs"], "best_frac_of_8tbs": round(best["gbs"] / 8000, 4), "runs": rows}
+
+
 def _sub_cfg(cfg, batch):
     from dataclasses import replace
     return replace(cfg, batch=batch)
@@ -304,6 +338,8 @@ def main():
     ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup (0: library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="measure the device's read ceiling (8 KiB blocks in random order) and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--bench-json", help="with --pmc-summary: a bench line of the workload (data-dependent bytes)")
@@ -321,6 +357,9 @@ def main():
     import paged_kv_cache_218_amd as pa
     from paged_kv_cache_218_amd.cache import PagedKVCache, lens_to_device, queries_to_device
 
+    if args.read_probe:
+        print(json.dumps({"read_probe": read_probe()}), flush=True)
+        return
     if args.workload in workloads.SPEC_CONFIGS:
         bench_spec(args)
         return

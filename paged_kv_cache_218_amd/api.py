@@ -237,6 +237,16 @@ def pa_spec_accept(p, q, draft, u_accept, u_draw, num_accepted, tokens, workspac
            "pa_spec_accept")
 
 
+# -- measurement aid -----------------------------------------------------------
+
+def pa_read_probe(buf, order, blocks_in_flight: int, workgroups: int, sink, stream=None) -> None:
+    """Read the device tensor `buf` (>= order.numel() * 8192 bytes) as 8 KiB
+    blocks in the order of the int32 device tensor `order`; sink: int32/uint32
+    device tensor of one element."""
+    _check(lib.pa_read_probe(_ptr(buf), int(order.numel()), _ptr(order), blocks_in_flight, workgroups,
+                             _ptr(sink), _stream(stream)), "pa_read_probe")
+
+
 # -- radix prefix cache -------------------------------------------------------
 
 def pa_prefix_cache_create(pool: Pool) -> PrefixCache:

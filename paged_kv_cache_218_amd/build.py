@@ -21,7 +21,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["attention.hip", "kvwrite.hip", "spec.hip"]
+HIP_SOURCES = ["attention.hip", "kvwrite.hip", "spec.hip", "probe.hip"]
 HOST_SOURCES = ["pool.cpp", "prefix_cache.cpp"]
 HIP_FLAGS = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1,0 +1,21 @@
+"""The read-bandwidth probe (a measurement aid for the HBM roofline) runs on
+the device: a full pass and a pass with out-of-range order entries, which are
+clamped to the last block, both complete and leave the sink untouched."""
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+def test_read_probe_passes():
+    import torch
+    import paged_kv_cache_218_amd as pa
+    n = 64
+    buf = torch.ones(n * 8192, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    order = torch.randperm(n, generator=torch.Generator().manual_seed(3)).to(torch.int32).cuda()
+    for depth in (1, 2, 4):
+        pa.pa_read_probe(buf, order, depth, 8, sink)
+    bad = torch.tensor([0, n, -1, 2 ** 30] * (n // 4), dtype=torch.int32, device="cuda")
+    pa.pa_read_probe(buf, bad, 2, 4, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
