@@ -104,15 +104,25 @@ def kernel_name(cfg, plan, desc) -> str:
     return f"{base}<{cfg.head_dim}, {cfg.block_size}, {nt}, {stream}, {kv8}, {tree}>"
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and with whitespace collapsed (string
+    and character literals kept as they are)."""
+    import re
+    token = re.compile(r"//[^\n]*|/\*.*?\*/|\"(?:\\.|[^\"\\])*\"|'(?:\\.|[^'\\])*'", re.S)
+    text = token.sub(lambda m: " " if m.group(0).startswith("/") else m.group(0), text)
+    return " ".join(text.split())
+
+
 def source_digest() -> str:
-    """sha256 of the HIP sources: counters taken on other sources are stale."""
+    """sha256 of the library's sources without comments or layout: counters
+    taken on other code are stale, an edit of comments alone keeps them."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_218_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".cpp")):
             h.update(f.encode())
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(_code_only(open(os.path.join(csrc, f), encoding="utf-8").read()).encode())
     return h.hexdigest()
 
 

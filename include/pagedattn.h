@@ -30,6 +30,13 @@
  *     synchronisation.
  *   - "host" pointers are CPU memory, "device" pointers are GPU memory on the
  *     current HIP device; all buffers are owned by the caller unless stated.
+ *   - Host bookkeeping memory is allocated when a pool or prefix cache is
+ *     made and by the calls that plan a write, match or insert a prefix, each
+ *     before it changes anything (PA_ERR_NO_MEMORY if that fails). Block
+ *     allocation, fork and release, eviction, the queries and destroying a
+ *     handle allocate nothing.
+ *   - A pool and its prefix cache are not safe for concurrent use: calls on
+ *     one pool are serialised by the caller. Distinct pools are independent.
  *   - Pool layout (device memory, caller-owned, element type = pool dtype):
  *       k_pool: [num_blocks][num_kv_heads][head_dim/32][block_size][32]
  *       v_pool: [num_blocks][num_kv_heads][head_dim][block_size]
@@ -72,7 +79,9 @@ enum {
   PA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head_dim, block_size, dtype, rows) */
   PA_ERR_NO_FREE_BLOCK = 3, /* the pool cannot supply the blocks asked for */
   PA_ERR_BAD_BLOCK = 4,     /* refcount underflow, fork/free of a free block */
-  PA_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
+  PA_ERR_HIP = 5,           /* a HIP runtime call or kernel launch failed */
+  PA_ERR_NO_MEMORY = 6      /* host memory for the bookkeeping could not be allocated;
+                               the call changed nothing */
 };
 
 enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1, PA_DTYPE_FP8_E4M3 = 2 };

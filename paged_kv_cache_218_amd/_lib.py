@@ -10,7 +10,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_NO_FREE_BLOCK, PA_ERR_BAD_BLOCK, PA_ERR_HIP = range(6)
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_NO_FREE_BLOCK, PA_ERR_BAD_BLOCK, PA_ERR_HIP, PA_ERR_NO_MEMORY = range(7)
 PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3 = 0, 1, 2
 PA_KV_SAME, PA_KV_FP8_E4M3 = 0, 1
 PA_PATH_AUTO, PA_PATH_VALU, PA_PATH_MFMA = 0, 1, 2

@@ -6,30 +6,44 @@
 // table, processed block by block with an online softmax (running maximum,
 // running sum of exponentials, rescaled accumulator).
 //
-// Work decomposition (one GPU):
-//   * a workgroup owns one (sequence b, KV head g, partition p) and all
-//     G*q_len query rows that read KV head g (GQA: query head h reads KV
-//     head h / G), so each K/V byte is read from HBM once per sequence;
-//   * a partition is a token range of partition_tokens; its wavefronts take
-//     32- or 64-token steps round-robin, each keeping its own online-softmax
-//     state, merged through LDS at the end;
-//   * with one partition per sequence the workgroup writes the output; with
-//     several, it writes (m, l, o) partials and the merge kernel combines them
-//     with the log-sum-exp identity (sequence-parallel attention: local
-//     attention per KV segment, then a reduction; "Mở rộng Quy mô và Triển
-//     khai", "Song song hóa Chuỗi").
+// Every (sequence b, KV head g) is one segment of work: all G*q_len query
+// rows that read KV head g (GQA: query head h reads KV head h / G) go through
+// the segment's tokens together, so each K/V byte is read from HBM once per
+// sequence. A wavefront takes 32-token steps (64 in the VALU kernel) and
+// keeps its own online-softmax state; the states of a workgroup's waves are
+// merged through LDS.
 //
-// Two main kernels:
-//   mfma_attn  bf16. Per 32-token step, scores S^T[token][row] come from
-//              v_mfma_f32_16x16x32_bf16 with the K rows as the A operand and
-//              the query rows as B; the output accumulator O^T[d][row] from
-//              the same instruction with the V^T slice as A and the bf16
-//              probabilities as B. Each lane owns one query row (lane % 16),
-//              so the softmax rescale is lane-local; only the per-step row
-//              maximum crosses lanes.
+// Two schedules:
+//   balanced    (default) the grid is the device's resident capacity; the
+//               (sequence, KV head, step) list is cut into one contiguous
+//               range per workgroup, equal in steps (prefix sums of the
+//               steps computed in every workgroup from context_lens). A
+//               segment inside one range is written directly; a segment cut
+//               by range boundaries leaves (m, l, o) partials, and the
+//               workgroup that counts the last piece in merges them with the
+//               log-sum-exp identity.
+//   partitions  a workgroup per (sequence, KV head, partition of
+//               partition_tokens tokens); partitions write partials and
+//               lse_merge combines them (sequence-parallel attention: local
+//               attention per KV segment, then a reduction; "Mở rộng Quy mô
+//               và Triển khai", "Song song hóa Chuỗi").
+//
+// Kernels:
+//   mfma_attn_balanced, mfma_attn  bf16 queries. Per 32-token step, scores
+//              S^T[token][row] come from v_mfma_f32_16x16x32_bf16 with the K
+//              rows as the A operand and the query rows as B; the output
+//              accumulator O^T[d][row] from the same instruction with the
+//              V^T slice as A and the bf16 probabilities as B. Each lane owns
+//              one query row (lane % 16), so the softmax rescale is
+//              lane-local; only the per-step row maximum crosses lanes. One
+//              or two 16-row tiles (NT). Template variants: FP8 E4M3 pools
+//              (KV8: codes converted to bf16 in registers, per-token scales on
+//              the scores and the P.V weights), tree masks over the drafted
+//              positions (TREE), non-temporal K/V loads (STREAM).
 //   valu_attn  f32 or bf16, any row count up to 16. One lane per token for
 //              the scores (query rows broadcast from LDS), probabilities
 //              through LDS, one lane per head-dim element for P.V.
+//   lse_merge  the partitions' merge.
 // Scores are kept in the base-2 domain (scale * log2(e) folded into one
 // multiplier) so every exponential is a single v_exp_f32.
 #include <hip/hip_runtime.h>
@@ -745,10 +759,7 @@ __device__ __forceinline__ int64_t owner(int64_t x, int64_t S, int64_t N) {
 }
 
 constexpr int kMergeBatch = 8;   // pieces whose partial loads a thread has in flight at once
-#ifndef PA_MIN_GROUP_STEPS
-#define PA_MIN_GROUP_STEPS 8
-#endif
-constexpr int kMinGroupSteps = PA_MIN_GROUP_STEPS;  // fewest steps a workgroup's range holds
+constexpr int kMinGroupSteps = 8;  // fewest steps a workgroup's range holds
 
 // The workgroup that completed a segment merges its npieces partials, which
 // start at piece p0 (log-sum-exp identity: out = sum_p w_p o_p / sum_p w_p
@@ -1270,7 +1281,7 @@ int ceil_div(int64_t x, int64_t y) { return int((x + y - 1) / y); }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS of one compute unit (gfx950)
-constexpr int kPerCuMinContext = 6144;  // longest context at which one workgroup per CU pays
+constexpr int kPerCuMinContext = 6144;  // one workgroup per CU once the longest context reaches this
 
 size_t lds_bytes(const Plan& pl, int D, int num_seqs) {
   if (pl.path == PA_PATH_MFMA) {

@@ -270,28 +270,30 @@ extern "C" pa_status pa_write_kv(pa_pool* pool, void* k_pool, void* v_pool,
                                  int32_t* block_table_host, int32_t table_capacity,
                                  int32_t* num_blocks_inout, int32_t start_pos, int32_t n_tokens,
                                  const void* k_new, const void* v_new, void* stream) {
-  if (!pool || !block_table_host || !num_blocks_inout) return PA_ERR_INVALID_ARG;
-  if (n_tokens > 0 && (!k_pool || !v_pool || !k_new || !v_new)) return PA_ERR_INVALID_ARG;
-  std::vector<int32_t> copies;
-  pa_status st = pa::plan_write(pool, block_table_host, table_capacity, num_blocks_inout,
-                                start_pos, n_tokens, &copies, INT32_MAX, nullptr);
-  if (st != PA_OK || n_tokens == 0) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int32_t n_pairs = static_cast<int32_t>(copies.size() / 2);
-  if (pool->dtype == PA_DTYPE_FP8_E4M3) {
-    if (n_pairs) st = launch_copies_fp8(pool, k_pool, v_pool, copies.data(), n_pairs, s);
-    if (st == PA_OK)
-      st = launch_scatter_fp8(pool, k_pool, v_pool, block_table_host, start_pos, n_tokens, k_new, v_new, s);
-  } else if (pool->dtype == PA_DTYPE_F32) {
-    if (n_pairs) st = launch_copies<float>(pool, k_pool, v_pool, copies.data(), n_pairs, s);
-    if (st == PA_OK)
-      st = launch_scatter<float>(pool, k_pool, v_pool, block_table_host, start_pos, n_tokens,
-                                 k_new, v_new, s);
-  } else {
-    if (n_pairs) st = launch_copies<uint16_t>(pool, k_pool, v_pool, copies.data(), n_pairs, s);
-    if (st == PA_OK)
-      st = launch_scatter<uint16_t>(pool, k_pool, v_pool, block_table_host, start_pos, n_tokens,
-                                    k_new, v_new, s);
-  }
-  return st;
+  return pa::guarded([&]() -> pa_status {
+    if (!pool || !block_table_host || !num_blocks_inout) return PA_ERR_INVALID_ARG;
+    if (n_tokens > 0 && (!k_pool || !v_pool || !k_new || !v_new)) return PA_ERR_INVALID_ARG;
+    std::vector<int32_t> copies;
+    pa_status st = pa::plan_write(pool, block_table_host, table_capacity, num_blocks_inout,
+                                  start_pos, n_tokens, &copies, INT32_MAX, nullptr);
+    if (st != PA_OK || n_tokens == 0) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int32_t n_pairs = static_cast<int32_t>(copies.size() / 2);
+    if (pool->dtype == PA_DTYPE_FP8_E4M3) {
+      if (n_pairs) st = launch_copies_fp8(pool, k_pool, v_pool, copies.data(), n_pairs, s);
+      if (st == PA_OK)
+        st = launch_scatter_fp8(pool, k_pool, v_pool, block_table_host, start_pos, n_tokens, k_new, v_new, s);
+    } else if (pool->dtype == PA_DTYPE_F32) {
+      if (n_pairs) st = launch_copies<float>(pool, k_pool, v_pool, copies.data(), n_pairs, s);
+      if (st == PA_OK)
+        st = launch_scatter<float>(pool, k_pool, v_pool, block_table_host, start_pos, n_tokens,
+                                   k_new, v_new, s);
+    } else {
+      if (n_pairs) st = launch_copies<uint16_t>(pool, k_pool, v_pool, copies.data(), n_pairs, s);
+      if (st == PA_OK)
+        st = launch_scatter<uint16_t>(pool, k_pool, v_pool, block_table_host, start_pos, n_tokens,
+                                      k_new, v_new, s);
+    }
+    return st;
+  });
 }

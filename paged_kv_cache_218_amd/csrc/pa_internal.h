@@ -3,6 +3,7 @@
 
 #include <cstdint>
 #include <climits>
+#include <new>
 #include <vector>
 
 #include "../../include/pagedattn.h"
@@ -36,6 +37,20 @@ void cache_unreferenced(pa_pool* p, int32_t block);      // a cached block's cou
 int64_t cache_reclaimable(const pa_pool* p);             // blocks eviction can still free
 int32_t cache_evict_one(pa_pool* p);                     // LRU unreferenced leaf, or -1
 void cache_release(pa_prefix_cache* c);                  // detach from the pool and delete
+
+// Run `body` (which returns a pa_status) so that no C++ exception crosses the
+// C interface: the only ones the standard containers used here throw are
+// allocation failures (bad_alloc, length_error), reported as
+// PA_ERR_NO_MEMORY. Every entry point that allocates does so before it
+// changes any state, so such a failure leaves the handle as it was.
+template <typename F>
+pa_status guarded(F&& body) noexcept {
+  try {
+    return body();
+  } catch (...) {
+    return PA_ERR_NO_MEMORY;
+  }
+}
 
 // Record a failed HIP call (this thread's last one, read by pa_last_hip_error)
 // and return PA_ERR_HIP. Defined with the HIP sources.

@@ -12,6 +12,7 @@
 // Pure C++ with no HIP dependency, so it is also built and sanitised on the
 // host alone.
 #include <cstring>
+#include <memory>
 #include <new>
 #include <vector>
 
@@ -25,6 +26,7 @@ extern "C" const char* pa_status_string(pa_status s) {
     case PA_ERR_NO_FREE_BLOCK: return "no free block in the pool";
     case PA_ERR_BAD_BLOCK: return "bad block (free block or refcount underflow)";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_NO_MEMORY: return "out of host memory";
     default: return "unknown status";
   }
 }
@@ -47,9 +49,10 @@ extern "C" int64_t pa_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_head
   return int64_t(2) * num_layers * num_kv_heads * head_dim * elem_bytes;
 }
 
-extern "C" pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
-                                    int32_t head_dim, int32_t dtype,
-                                    const int32_t* initial_free_order, pa_pool** out) {
+namespace {
+
+pa_status pool_create(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t dtype, const int32_t* initial_free_order, pa_pool** out) {
   if (!out) return PA_ERR_INVALID_ARG;
   *out = nullptr;
   if (num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
@@ -58,8 +61,7 @@ extern "C" pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, int3
     return PA_ERR_UNSUPPORTED;
   if (!pa::supported_block_size(block_size) || !pa::supported_head_dim(head_dim))
     return PA_ERR_UNSUPPORTED;
-  pa_pool* p = new (std::nothrow) pa_pool();
-  if (!p) return PA_ERR_INVALID_ARG;
+  std::unique_ptr<pa_pool> p(new pa_pool());
   p->num_blocks = num_blocks;
   p->block_size = block_size;
   p->num_kv_heads = num_kv_heads;
@@ -70,18 +72,26 @@ extern "C" pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, int3
   std::vector<char> seen(num_blocks, 0);
   for (int32_t i = 0; i < num_blocks; ++i) {
     int32_t b = initial_free_order ? initial_free_order[i] : i;
-    if (b < 0 || b >= num_blocks || seen[b]) {
-      delete p;
-      return PA_ERR_INVALID_ARG;
-    }
+    if (b < 0 || b >= num_blocks || seen[b]) return PA_ERR_INVALID_ARG;
     seen[b] = 1;
     // stack top (back) is the head of the free list
     p->stack[num_blocks - 1 - i] = b;
   }
-  *out = p;
+  *out = p.release();
   return PA_OK;
 }
 
+}  // namespace
+
+extern "C" pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t dtype,
+                                    const int32_t* initial_free_order, pa_pool** out) {
+  return pa::guarded([&] {
+    return pool_create(num_blocks, block_size, num_kv_heads, head_dim, dtype, initial_free_order, out);
+  });
+}
+
+// Releasing a pool (and its cache) allocates nothing.
 extern "C" void pa_pool_destroy(pa_pool* pool) {
   if (!pool) return;
   if (pool->cache) pa::cache_release(pool->cache);
@@ -202,6 +212,7 @@ pa_status plan_write(pa_pool* p, int32_t* table, int32_t capacity, int32_t* live
   need += n_copy;
   if (copies && n_copy > max_copies) return PA_ERR_INVALID_ARG;
   if (!can_supply(p, need)) return PA_ERR_NO_FREE_BLOCK;
+  if (copies) copies->reserve(size_t(2 * n_copy));  // the only allocation, before any change
 
   for (int32_t j = first_block; j <= last; ++j) {
     if (j < live) {
@@ -236,15 +247,17 @@ extern "C" pa_status pa_write_plan(pa_pool* pool, int32_t* block_table, int32_t 
                                    int32_t* num_blocks_inout, int32_t start_pos,
                                    int32_t n_tokens, int32_t* copies_out, int32_t max_copies,
                                    int32_t* n_copies_out, int32_t* slots_out) {
-  std::vector<int32_t> copies;
-  const int32_t cap = copies_out ? max_copies : INT32_MAX;
-  pa_status st = pa::plan_write(pool, block_table, table_capacity, num_blocks_inout, start_pos,
-                                n_tokens, &copies, cap, slots_out);
-  if (st != PA_OK) return st;
-  const int32_t n = static_cast<int32_t>(copies.size() / 2);
-  if (n_copies_out) *n_copies_out = n;
-  if (copies_out && n) std::memcpy(copies_out, copies.data(), copies.size() * sizeof(int32_t));
-  return PA_OK;
+  return pa::guarded([&]() -> pa_status {
+    std::vector<int32_t> copies;
+    const int32_t cap = copies_out ? max_copies : INT32_MAX;
+    const pa_status st = pa::plan_write(pool, block_table, table_capacity, num_blocks_inout, start_pos,
+                                        n_tokens, &copies, cap, slots_out);
+    if (st != PA_OK) return st;
+    const int32_t n = static_cast<int32_t>(copies.size() / 2);
+    if (n_copies_out) *n_copies_out = n;
+    if (copies_out && n) std::memcpy(copies_out, copies.data(), copies.size() * sizeof(int32_t));
+    return PA_OK;
+  });
 }
 
 // Ancestor masks of a tree of drafted tokens: bit j of masks[i] is set when

@@ -18,12 +18,83 @@
 // Pure C++, no HIP: built and sanitised on the host alone.
 #include <algorithm>
 #include <map>
+#include <memory>
 #include <new>
 #include <set>
 #include <utility>
 #include <vector>
 
 #include "pa_internal.h"
+
+namespace {
+
+// Blocks ordered by (stamp, block id): an indexed binary min-heap with room
+// for every block of the pool, allocated with the cache, so that the pool
+// operations that reach it (a release, an allocation that evicts) never
+// allocate. The stamps of the blocks it holds do not change while they are in.
+class BlockHeap {
+ public:
+  void init(size_t num_blocks, const std::vector<int64_t>* stamps) {
+    heap_.assign(num_blocks, -1);
+    pos_.assign(num_blocks, -1);
+    size_ = 0;
+    stamp_ = stamps;
+  }
+  bool empty() const { return size_ == 0; }
+  int32_t top() const { return size_ > 0 ? heap_[0] : -1; }
+  void insert(int32_t b) {
+    if (pos_[b] >= 0) return;
+    heap_[size_] = b;
+    pos_[b] = size_;
+    up(size_++);
+  }
+  void erase(int32_t b) {
+    const int32_t i = pos_[b];
+    if (i < 0) return;
+    pos_[b] = -1;
+    if (i == --size_) return;
+    const int32_t moved = heap_[size_];
+    heap_[i] = moved;
+    pos_[moved] = i;
+    up(i);
+    down(pos_[moved]);
+  }
+
+ private:
+  bool before(int32_t a, int32_t b) const {
+    const int64_t sa = (*stamp_)[a], sb = (*stamp_)[b];
+    return sa < sb || (sa == sb && a < b);
+  }
+  void swap_at(int32_t i, int32_t j) {
+    std::swap(heap_[i], heap_[j]);
+    pos_[heap_[i]] = i;
+    pos_[heap_[j]] = j;
+  }
+  void up(int32_t i) {
+    while (i > 0) {
+      const int32_t par = (i - 1) / 2;
+      if (!before(heap_[i], heap_[par])) break;
+      swap_at(i, par);
+      i = par;
+    }
+  }
+  void down(int32_t i) {
+    for (;;) {
+      const int32_t l = 2 * i + 1, r = l + 1;
+      int32_t m = i;
+      if (l < size_ && before(heap_[l], heap_[m])) m = l;
+      if (r < size_ && before(heap_[r], heap_[m])) m = r;
+      if (m == i) return;
+      swap_at(i, m);
+      i = m;
+    }
+  }
+  std::vector<int32_t> heap_, pos_;
+  int32_t size_ = 0;
+  const std::vector<int64_t>* stamp_ = nullptr;
+};
+
+}  // namespace
 
 struct pa_prefix_cache {
   pa_pool* pool = nullptr;
@@ -34,7 +105,10 @@ struct pa_prefix_cache {
   std::vector<std::map<std::vector<int32_t>, int32_t>> children;  // per block
   std::map<std::vector<int32_t>, int32_t> roots;                  // children of the root
   std::vector<int64_t> stamp;             // per block: when it became unreferenced, or -1
-  std::set<std::pair<int64_t, int32_t>> leaves;  // unreferenced leaves by (stamp, block)
+  BlockHeap leaves;                       // unreferenced leaves by (stamp, block)
+  // scratch of cache_reclaimable, sized for every block when the cache is made
+  std::vector<int32_t> walk_order, walk_stack;
+  std::vector<char> walk_live;
 };
 
 namespace {
@@ -45,19 +119,19 @@ std::map<std::vector<int32_t>, int32_t>& children_of(pa_prefix_cache* c, int32_t
 
 // Take block b (an unreferenced leaf) out of the tree.
 void detach(pa_prefix_cache* c, int32_t b) {
-  c->leaves.erase({c->stamp[b], b});
+  c->leaves.erase(b);
   const int32_t par = c->parent[b];
   children_of(c, par).erase(c->key[b]);
   c->cached[b] = 0;
   c->parent[b] = -1;
   c->key[b].clear();
   c->stamp[b] = -1;
-  if (par >= 0 && c->stamp[par] >= 0 && c->children[par].empty()) c->leaves.insert({c->stamp[par], par});
+  if (par >= 0 && c->stamp[par] >= 0 && c->children[par].empty()) c->leaves.insert(par);
 }
 
 int32_t evict_one(pa_prefix_cache* c) {
   if (c->leaves.empty()) return -1;
-  const int32_t b = c->leaves.begin()->second;
+  const int32_t b = c->leaves.top();
   detach(c, b);
   return b;
 }
@@ -71,14 +145,20 @@ bool cache_holds(const pa_pool* p, int32_t b) { return p->cache->cached[b] != 0;
 void cache_unreferenced(pa_pool* p, int32_t b) {
   pa_prefix_cache* c = p->cache;
   c->stamp[b] = ++c->clock;
-  if (c->children[b].empty()) c->leaves.insert({c->stamp[b], b});
+  if (c->children[b].empty()) c->leaves.insert(b);
 }
 
 // Unreferenced blocks with no referenced block below them: children are
 // visited before their parents (iterative, the tree can be deep).
+// No allocation: the walk uses the cache's preallocated scratch (each cached
+// block enters the stack and the order once).
 int64_t cache_reclaimable(const pa_pool* p) {
-  const pa_prefix_cache* c = p->cache;
-  std::vector<int32_t> order, stack;
+  pa_prefix_cache* c = p->cache;
+  std::vector<int32_t>& order = c->walk_order;
+  std::vector<int32_t>& stack = c->walk_stack;
+  std::vector<char>& live = c->walk_live;
+  order.clear();
+  stack.clear();
   for (const auto& kv : c->roots) stack.push_back(kv.second);
   while (!stack.empty()) {
     const int32_t n = stack.back();
@@ -86,7 +166,7 @@ int64_t cache_reclaimable(const pa_pool* p) {
     order.push_back(n);
     for (const auto& kv : c->children[n]) stack.push_back(kv.second);
   }
-  std::vector<char> live(c->cached.size(), 0);
+  std::fill(live.begin(), live.end(), 0);
   int64_t count = 0;
   for (auto it = order.rbegin(); it != order.rend(); ++it) {
     const int32_t n = *it;
@@ -106,11 +186,12 @@ void cache_release(pa_prefix_cache* c) {
   // unreferenced cached block (ascending stamp); referenced ones go back to
   // the free list when their holders release them
   for (int32_t b = evict_one(c); b >= 0; b = evict_one(c)) p->stack.push_back(b);
-  std::vector<std::pair<int64_t, int32_t>> rest;
   for (int32_t b = 0; b < p->num_blocks; ++b)
-    if (c->cached[b] && c->stamp[b] >= 0) rest.push_back({c->stamp[b], b});
-  std::sort(rest.begin(), rest.end());
-  for (const auto& sb : rest) p->stack.push_back(sb.second);
+    if (c->cached[b] && c->stamp[b] >= 0) c->leaves.insert(b);
+  for (int32_t b = c->leaves.top(); b >= 0; b = c->leaves.top()) {
+    c->leaves.erase(b);
+    p->stack.push_back(b);
+  }
   p->cache = nullptr;
   delete c;
 }
@@ -121,18 +202,23 @@ extern "C" pa_status pa_prefix_cache_create(pa_pool* pool, pa_prefix_cache** out
   if (!pool || !out) return PA_ERR_INVALID_ARG;
   *out = nullptr;
   if (pool->cache) return PA_ERR_INVALID_ARG;  // one cache per pool
-  pa_prefix_cache* c = new (std::nothrow) pa_prefix_cache();
-  if (!c) return PA_ERR_INVALID_ARG;
-  const size_t nb = size_t(pool->num_blocks);
-  c->pool = pool;
-  c->cached.assign(nb, 0);
-  c->parent.assign(nb, -1);
-  c->key.assign(nb, {});
-  c->children.assign(nb, {});
-  c->stamp.assign(nb, -1);
-  pool->cache = c;
-  *out = c;
-  return PA_OK;
+  return pa::guarded([&]() -> pa_status {
+    std::unique_ptr<pa_prefix_cache> c(new pa_prefix_cache());
+    const size_t nb = size_t(pool->num_blocks);
+    c->pool = pool;
+    c->cached.assign(nb, 0);
+    c->parent.assign(nb, -1);
+    c->key.assign(nb, {});
+    c->children.assign(nb, {});
+    c->stamp.assign(nb, -1);
+    c->leaves.init(nb, &c->stamp);
+    c->walk_order.reserve(nb);
+    c->walk_stack.reserve(nb);
+    c->walk_live.assign(nb, 0);
+    pool->cache = c.get();
+    *out = c.release();
+    return PA_OK;
+  });
 }
 
 extern "C" void pa_prefix_cache_destroy(pa_prefix_cache* cache) {
@@ -144,79 +230,91 @@ extern "C" pa_status pa_prefix_match(pa_prefix_cache* cache, const int32_t* toke
   if (!cache || !n_blocks || n_tokens < 0 || capacity < 0 || (n_tokens > 0 && !tokens) ||
       (capacity > 0 && !table))
     return PA_ERR_INVALID_ARG;
-  pa_pool* p = cache->pool;
-  const int32_t bs = p->block_size;
-  std::vector<int32_t> chunk(bs);
-  int32_t node = -1, n = 0;
-  const int32_t most = std::min(n_tokens / bs, capacity);
-  for (; n < most; ++n) {
-    chunk.assign(tokens + int64_t(n) * bs, tokens + int64_t(n + 1) * bs);
-    auto& kids = children_of(cache, node);
-    const auto it = kids.find(chunk);
-    if (it == kids.end()) break;
-    node = it->second;
-    table[n] = node;
-  }
-  for (int32_t i = 0; i < n; ++i) {  // fork the matched blocks, reviving unreferenced ones
-    const int32_t b = table[i];
-    if (p->refcount[b] == 0) {
-      cache->leaves.erase({cache->stamp[b], b});
-      cache->stamp[b] = -1;
+  return pa::guarded([&]() -> pa_status {
+    pa_pool* p = cache->pool;
+    const int32_t bs = p->block_size;
+    std::vector<int32_t> chunk(bs);  // the only allocation, before any change
+    int32_t node = -1, n = 0;
+    const int32_t most = std::min(n_tokens / bs, capacity);
+    for (; n < most; ++n) {
+      chunk.assign(tokens + int64_t(n) * bs, tokens + int64_t(n + 1) * bs);
+      auto& kids = children_of(cache, node);
+      const auto it = kids.find(chunk);
+      if (it == kids.end()) break;
+      node = it->second;
+      table[n] = node;
     }
-    ++p->refcount[b];
-  }
-  *n_blocks = n;
-  return PA_OK;
+    for (int32_t i = 0; i < n; ++i) {  // fork the matched blocks, reviving unreferenced ones
+      const int32_t b = table[i];
+      if (p->refcount[b] == 0) {
+        cache->leaves.erase(b);
+        cache->stamp[b] = -1;
+      }
+      ++p->refcount[b];
+    }
+    *n_blocks = n;
+    return PA_OK;
+  });
 }
 
 extern "C" pa_status pa_prefix_insert(pa_prefix_cache* cache, const int32_t* tokens, int32_t n_tokens,
                                       const int32_t* table, int32_t n_blocks, int32_t* n_new) {
   if (!cache || n_tokens < 0 || n_blocks < 0 || (n_tokens > 0 && !tokens) || (n_blocks > 0 && !table))
     return PA_ERR_INVALID_ARG;
-  pa_pool* p = cache->pool;
-  const int32_t bs = p->block_size;
-  const int32_t n = std::min(n_blocks, n_tokens / bs);
-  struct Planned {
-    int32_t parent;
-    std::vector<int32_t> chunk;
-    int32_t block;
-  };
-  std::vector<Planned> plan;
-  std::set<int32_t> planned;
-  int32_t node = -1;
-  bool fresh = false;  // below a planned node: nothing cached yet
-  for (int32_t i = 0; i < n; ++i) {
-    std::vector<int32_t> chunk(tokens + int64_t(i) * bs, tokens + int64_t(i + 1) * bs);
-    int32_t child = -1;
-    if (!fresh) {
-      auto& kids = children_of(cache, node);
-      const auto it = kids.find(chunk);
-      if (it != kids.end()) child = it->second;
+  return pa::guarded([&]() -> pa_status {
+    pa_pool* p = cache->pool;
+    const int32_t bs = p->block_size;
+    const int32_t n = std::min(n_blocks, n_tokens / bs);
+    // Everything the insertion needs is allocated while planning (the tree
+    // node, with its key, and the block's own copy of the key), so that
+    // applying the plan allocates nothing and cannot stop half way.
+    using Children = std::map<std::vector<int32_t>, int32_t>;
+    struct Planned {
+      int32_t parent;
+      Children::node_type node;
+      std::vector<int32_t> key;
+      int32_t block;
+    };
+    std::vector<Planned> plan;
+    plan.reserve(size_t(n));
+    std::set<int32_t> planned;
+    int32_t node = -1;
+    bool fresh = false;  // below a planned node: nothing cached yet
+    for (int32_t i = 0; i < n; ++i) {
+      std::vector<int32_t> chunk(tokens + int64_t(i) * bs, tokens + int64_t(i + 1) * bs);
+      int32_t child = -1;
+      if (!fresh) {
+        auto& kids = children_of(cache, node);
+        const auto it = kids.find(chunk);
+        if (it != kids.end()) child = it->second;
+      }
+      if (child >= 0) {
+        node = child;
+        continue;
+      }
+      const int32_t b = table[i];
+      if (b < 0 || b >= p->num_blocks) return PA_ERR_INVALID_ARG;
+      if (p->refcount[b] == 0) return PA_ERR_BAD_BLOCK;
+      if (cache->cached[b] || planned.count(b)) return PA_ERR_INVALID_ARG;  // cached under another prefix
+      Children holder;
+      holder.emplace(chunk, b);
+      plan.push_back({node, holder.extract(holder.begin()), std::move(chunk), b});
+      planned.insert(b);
+      node = b;
+      fresh = true;
     }
-    if (child >= 0) {
-      node = child;
-      continue;
+    for (auto& pl : plan) {
+      if (pl.parent >= 0 && cache->stamp[pl.parent] >= 0 && cache->children[pl.parent].empty())
+        cache->leaves.erase(pl.parent);  // no longer a leaf
+      cache->cached[pl.block] = 1;
+      cache->parent[pl.block] = pl.parent;
+      cache->key[pl.block] = std::move(pl.key);
+      cache->stamp[pl.block] = -1;
+      children_of(cache, pl.parent).insert(std::move(pl.node));
     }
-    const int32_t b = table[i];
-    if (b < 0 || b >= p->num_blocks) return PA_ERR_INVALID_ARG;
-    if (p->refcount[b] == 0) return PA_ERR_BAD_BLOCK;
-    if (cache->cached[b] || planned.count(b)) return PA_ERR_INVALID_ARG;  // cached under another prefix
-    plan.push_back({node, std::move(chunk), b});
-    planned.insert(b);
-    node = b;
-    fresh = true;
-  }
-  for (auto& pl : plan) {
-    if (pl.parent >= 0 && cache->stamp[pl.parent] >= 0 && cache->children[pl.parent].empty())
-      cache->leaves.erase({cache->stamp[pl.parent], pl.parent});  // no longer a leaf
-    cache->cached[pl.block] = 1;
-    cache->parent[pl.block] = pl.parent;
-    cache->key[pl.block] = pl.chunk;
-    cache->stamp[pl.block] = -1;
-    children_of(cache, pl.parent)[pl.chunk] = pl.block;
-  }
-  if (n_new) *n_new = int32_t(plan.size());
-  return PA_OK;
+    if (n_new) *n_new = int32_t(plan.size());
+    return PA_OK;
+  });
 }
 
 extern "C" pa_status pa_prefix_evict(pa_prefix_cache* cache, int32_t max_blocks, int32_t* evicted,

@@ -10,10 +10,26 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <new>
 #include <random>
 #include <vector>
 
 #include "../../include/pagedattn.h"
+
+// Every operator new of the program is counted, so that the pool and cache
+// operations that must not allocate (a release, an allocation, an eviction,
+// the statistics, destroying the pool) can be checked to allocate nothing.
+static long g_news = 0;
+void* operator new(std::size_t n) {
+  ++g_news;
+  if (void* p = std::malloc(n ? n : 1)) return p;
+  throw std::bad_alloc();
+}
+void* operator new[](std::size_t n) { return operator new(n); }
+void operator delete(void* p) noexcept { std::free(p); }
+void operator delete[](void* p) noexcept { std::free(p); }
+void operator delete(void* p, std::size_t) noexcept { std::free(p); }
+void operator delete[](void* p, std::size_t) noexcept { std::free(p); }
 
 #define CHECK(c)                                                        \
   do {                                                                  \
@@ -21,6 +37,14 @@
       std::fprintf(stderr, "check failed line %d: %s\n", __LINE__, #c); \
       std::exit(1);                                                     \
     }                                                                   \
+  } while (0)
+
+// expr runs without a single operator new
+#define NO_ALLOC(expr)            \
+  do {                            \
+    const long news0 = g_news;    \
+    expr;                         \
+    CHECK(g_news == news0);       \
   } while (0)
 
 // Requests sharing a few prompts against a pool with a prefix cache: match,
@@ -33,7 +57,9 @@ static void prefix_cache_stress() {
   pa_pool* pool = nullptr;
   CHECK(pa_pool_create(NB, BS, 2, 64, PA_DTYPE_BF16, nullptr, &pool) == PA_OK);
   pa_prefix_cache* cache = nullptr;
+  const long news_before_cache = g_news;
   CHECK(pa_prefix_cache_create(pool, &cache) == PA_OK);
+  CHECK(g_news > news_before_cache);  // the counting operator new is the one in use
   std::vector<std::vector<int32_t>> prompts(4);
   for (auto& pr : prompts) {
     pr.resize(BS * (1 + rng() % 5) + rng() % BS);
@@ -71,9 +97,15 @@ static void prefix_cache_stress() {
       CHECK(st == PA_OK || st == PA_ERR_NO_FREE_BLOCK);
     } else if (op == 2) {
       int32_t ev[8], n = 0;
-      CHECK(pa_prefix_evict(cache, int32_t(rng() % 8), ev, &n) == PA_OK);
+      NO_ALLOC(CHECK(pa_prefix_evict(cache, int32_t(rng() % 8), ev, &n) == PA_OK));
+    } else if (op == 3) {  // a block taken and given back: may evict, never allocates
+      int32_t b = -1;
+      pa_status st = PA_OK;
+      NO_ALLOC(st = pa_block_alloc(pool, &b));
+      CHECK(st == PA_OK || st == PA_ERR_NO_FREE_BLOCK);
+      if (st == PA_OK) NO_ALLOC(CHECK(pa_block_free(pool, b) == PA_OK));
     } else {  // finish
-      for (int j = 0; j < live[s]; ++j) CHECK(pa_block_free(pool, tables[s][j]) == PA_OK);
+      for (int j = 0; j < live[s]; ++j) NO_ALLOC(CHECK(pa_block_free(pool, tables[s][j]) == PA_OK));
       tables[s].assign(CAP, -1);
       live[s] = 0;
     }
@@ -83,7 +115,7 @@ static void prefix_cache_stress() {
         for (int j = 0; j < live[q]; ++j) ++held[tables[q][j]];
       int32_t nfree = 0, cached = 0, unref = 0, recl = 0;
       CHECK(pa_pool_num_free(pool, &nfree) == PA_OK);
-      CHECK(pa_prefix_cache_stats(cache, &cached, &unref, &recl) == PA_OK);
+      NO_ALLOC(CHECK(pa_prefix_cache_stats(cache, &cached, &unref, &recl) == PA_OK));
       int referenced = 0;
       for (int b = 0; b < NB; ++b) {
         int32_t rc = -1;
@@ -94,7 +126,7 @@ static void prefix_cache_stress() {
       CHECK(nfree + unref + referenced == NB && recl <= unref);
     }
   }
-  pa_pool_destroy(pool);  // also destroys the attached cache
+  NO_ALLOC(pa_pool_destroy(pool));  // also destroys the attached cache
 }
 
 int main() {

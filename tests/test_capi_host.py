@@ -31,8 +31,9 @@ def test_every_declared_function_is_exported():
 
 
 def test_status_strings():
-    for s in range(6):
-        assert pa.pa_status_string(s)
+    for s in range(7):
+        assert pa.pa_status_string(s) != "unknown status"
+    assert pa.pa_status_string(_lib.PA_ERR_NO_MEMORY) == "out of host memory"
     assert pa.pa_status_string(99) == "unknown status"
 
 
