@@ -20,8 +20,16 @@
 // operations that must not allocate (a release, an allocation, an eviction,
 // the statistics, destroying the pool) can be checked to allocate nothing.
 static long g_news = 0;
+// Fault injection: with g_fail_in = k >= 0, k more allocations succeed and
+// the next one throws std::bad_alloc (then injection is off again).
+static long g_fail_in = -1;
 void* operator new(std::size_t n) {
   ++g_news;
+  if (g_fail_in == 0) {
+    g_fail_in = -1;
+    throw std::bad_alloc();
+  }
+  if (g_fail_in > 0) --g_fail_in;
   if (void* p = std::malloc(n ? n : 1)) return p;
   throw std::bad_alloc();
 }
@@ -129,6 +137,142 @@ static void prefix_cache_stress() {
   NO_ALLOC(pa_pool_destroy(pool));  // also destroys the attached cache
 }
 
+// Every entry point that allocates, made to fail at each of its allocations in
+// turn: it must return PA_ERR_NO_MEMORY and leave the pool, the cache and the
+// caller's table exactly as they were (and leak nothing: LeakSanitizer runs
+// at exit).
+struct World {
+  pa_pool* pool = nullptr;
+  pa_prefix_cache* cache = nullptr;
+  std::vector<int32_t> table, toks;
+  int32_t live = 0;
+};
+
+static const int kFNB = 40, kFBS = 16, kFCAP = 8;
+
+// The same state every time: two requests cached and finished, one request
+// holding a matched prefix and its own blocks.
+static World make_world() {
+  World w;
+  CHECK(pa_pool_create(kFNB, kFBS, 2, 64, PA_DTYPE_BF16, nullptr, &w.pool) == PA_OK);
+  CHECK(pa_prefix_cache_create(w.pool, &w.cache) == PA_OK);
+  for (int r = 0; r < 2; ++r) {
+    std::vector<int32_t> toks(kFBS * 3 + 5), tab(kFCAP, -1);
+    for (size_t i = 0; i < toks.size(); ++i) toks[i] = int32_t((i * 7 + r * (i >= kFBS ? 1 : 0)) % 5);
+    int32_t lv = 0, added = 0;
+    CHECK(pa_write_plan(w.pool, tab.data(), kFCAP, &lv, 0, int32_t(toks.size()), nullptr, 0, nullptr, nullptr) == PA_OK);
+    CHECK(pa_prefix_insert(w.cache, toks.data(), int32_t(toks.size()), tab.data(), lv, &added) == PA_OK);
+    for (int j = 0; j < lv; ++j) CHECK(pa_block_free(w.pool, tab[j]) == PA_OK);
+  }
+  w.toks.resize(kFBS * 4 + 3);
+  for (size_t i = 0; i < w.toks.size(); ++i) w.toks[i] = int32_t((i * 7) % 5);
+  w.table.assign(kFCAP, -1);
+  int32_t n = 0;
+  CHECK(pa_prefix_match(w.cache, w.toks.data(), int32_t(w.toks.size()), w.table.data(), kFCAP, &n) == PA_OK);
+  w.live = n;
+  CHECK(pa_write_plan(w.pool, w.table.data(), kFCAP, &w.live, n * kFBS, int32_t(w.toks.size()) - n * kFBS,
+                      nullptr, 0, nullptr, nullptr) == PA_OK);
+  return w;
+}
+
+struct Snapshot {
+  std::vector<int32_t> rc, fl, blocks, parents, table;
+  std::vector<int64_t> stamps;
+  int32_t live = 0;
+  bool operator==(const Snapshot& o) const {
+    return rc == o.rc && fl == o.fl && blocks == o.blocks && parents == o.parents && stamps == o.stamps &&
+           table == o.table && live == o.live;
+  }
+};
+
+static Snapshot snap(const World& w) {
+  Snapshot s;
+  s.rc.assign(kFNB, 0);
+  for (int b = 0; b < kFNB; ++b) CHECK(pa_block_refcount(w.pool, b, &s.rc[b]) == PA_OK);
+  int32_t n = 0;
+  s.fl.assign(kFNB, -1);
+  CHECK(pa_pool_free_list(w.pool, s.fl.data(), kFNB, &n) == PA_OK);
+  s.fl.resize(n);
+  s.blocks.assign(kFNB, 0);
+  s.parents.assign(kFNB, 0);
+  s.stamps.assign(kFNB, 0);
+  CHECK(pa_prefix_cache_dump(w.cache, s.blocks.data(), s.parents.data(), s.stamps.data(), kFNB, &n) == PA_OK);
+  s.blocks.resize(n);
+  s.parents.resize(n);
+  s.stamps.resize(n);
+  s.table = w.table;
+  s.live = w.live;
+  return s;
+}
+
+static void fault_injection() {
+  // each call, run on a fresh copy of the same state with the k-th allocation failing
+  auto probe = [](const char* what, auto call) {
+    for (long k = 0;; ++k) {
+      World w = make_world();
+      const Snapshot before = snap(w);
+      const pa_status st = call(w, k);  // arms the injection right before the call under test
+      const bool injected = g_fail_in == -1;
+      g_fail_in = -1;
+      if (injected) {
+        if (st != PA_ERR_NO_MEMORY || !(snap(w) == before)) {
+          std::fprintf(stderr, "%s: allocation %ld failing gave status %d or changed the state\n", what, k, st);
+          std::exit(1);
+        }
+      } else {
+        CHECK(st == PA_OK);  // needed at most k allocations: the call ran to the end
+        CHECK(k > 0);        // and it did allocate, so the failures were exercised
+        std::printf("%s: each of %ld allocations failing left the state unchanged\n", what, k);
+        pa_pool_destroy(w.pool);
+        break;
+      }
+      pa_pool_destroy(w.pool);
+      CHECK(k < 10000);
+    }
+  };
+  probe("pa_write_plan (rewrite of cached blocks)", [](World& w, long k) {
+    std::vector<int32_t> copies(2 * kFCAP);
+    int32_t ncp = 0;
+    g_fail_in = k;
+    return pa_write_plan(w.pool, w.table.data(), kFCAP, &w.live, 0, 2 * kFBS, copies.data(), kFCAP, &ncp, nullptr);
+  });
+  probe("pa_prefix_match", [](World& w, long k) {
+    std::vector<int32_t> t(kFCAP, -1);
+    int32_t n = 0;
+    g_fail_in = k;
+    return pa_prefix_match(w.cache, w.toks.data(), int32_t(w.toks.size()), t.data(), kFCAP, &n);
+  });
+  probe("pa_prefix_insert", [](World& w, long k) {
+    int32_t added = 0;
+    g_fail_in = k;
+    return pa_prefix_insert(w.cache, w.toks.data(), int32_t(w.toks.size()), w.table.data(), w.live, &added);
+  });
+  probe("pa_pool_create", [](World&, long k) {
+    pa_pool* p = nullptr;
+    g_fail_in = k;
+    const pa_status st = pa_pool_create(kFNB, kFBS, 2, 64, PA_DTYPE_BF16, nullptr, &p);
+    const long left = g_fail_in;
+    g_fail_in = -1;
+    CHECK((st == PA_OK) == (p != nullptr));
+    if (p) pa_pool_destroy(p);
+    g_fail_in = left;
+    return st;
+  });
+  probe("pa_prefix_cache_create", [](World&, long k) {
+    pa_pool* p = nullptr;
+    CHECK(pa_pool_create(kFNB, kFBS, 2, 64, PA_DTYPE_BF16, nullptr, &p) == PA_OK);
+    pa_prefix_cache* c = nullptr;
+    g_fail_in = k;
+    const pa_status st = pa_prefix_cache_create(p, &c);
+    const long left = g_fail_in;
+    g_fail_in = -1;
+    CHECK((st == PA_OK) == (c != nullptr));
+    pa_pool_destroy(p);
+    g_fail_in = left;
+    return st;
+  });
+}
+
 int main() {
   const int NB = 96, BS = 16, CAP = 24, NSEQ = 8;
   std::mt19937 rng(218);
@@ -232,6 +376,7 @@ int main() {
   }
   pa_pool_destroy(pool);
   prefix_cache_stress();
+  fault_injection();
   std::printf("pool stress ok\n");
   return 0;
 }
