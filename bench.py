@@ -199,6 +199,86 @@ def _pmc_finish(out, fetch_dir, write_dir, copy_bytes, kernel, workload):
     print(json.dumps(out, indent=1))
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published (no sparsity)
+SIMD_CLOCK_GHZ = 2.4             # MI355X peak engine clock
+
+
+def counter_summary(workload: str, run_dirs, bench_json: str):
+    """Per-launch means of the main kernel's rocprofv3 --pmc counters (one or
+    more runs of bench.py, derived metrics such as MfmaUtil, MfmaFlopsBF16,
+    VALUBusy, OccupancyPercent allowed) written to
+    profiles/counters_<workload>.json, stamped with the source digest.
+    bench_json: a bench line of the same workload, whose launch time turns the
+    MFMA flops per launch into a rate; its kernel name selects the dispatches."""
+    import csv
+    import statistics
+    rec = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    kernel = rec["roofline"]["kernel"]
+    launch_us = rec["roofline"]["launch_us"]
+    values, regs = {}, {}
+    for d in run_dirs:
+        rows = [r for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv")))
+                if kernel in r["Kernel_Name"]]
+        if not rows:
+            raise SystemExit(f"{d}: no {kernel} dispatches")
+        for r in rows:
+            values.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            for key in ("VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "LDS_Block_Size", "Workgroup_Size"):
+                if r.get(key) not in (None, ""):
+                    regs[key] = int(float(r[key]))
+    out = {"workload": workload, "kernel": kernel, "source_sha256": source_digest(),
+           "launch_us": launch_us, "dispatches": {k: len(v) for k, v in values.items()},
+           "per_launch": {k: statistics.mean(v) for k, v in values.items()}, "kernel_resources": regs}
+    flops = out["per_launch"].get("MfmaFlopsBF16")
+    if flops is not None:
+        tflops = flops / (launch_us * 1e-6) / 1e12
+        out["mfma_bf16_tflops"] = tflops
+        out["mfma_bf16_frac_of_peak"] = tflops / MFMA_BF16_PEAK_TFLOPS
+        if "flops" in rec:
+            out["algorithmic_flops"] = rec["flops"]
+            out["mfma_flops_over_algorithmic"] = flops / rec["flops"]
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def committed_counters(workload: str, kernel: str):
+    """MFMA and VALU utilisation of the main kernel from committed rocprofv3
+    counter runs, if they were taken on the current sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != source_digest() or rec.get("kernel") != kernel:
+        return None
+    pl = rec["per_launch"]
+    keep = {"mfma_util_pct": pl.get("MfmaUtil"), "mfma_bf16_tflops": rec.get("mfma_bf16_tflops"),
+            "mfma_bf16_frac_of_peak": rec.get("mfma_bf16_frac_of_peak"), "valu_busy_pct": pl.get("VALUBusy"),
+            "occupancy_pct": pl.get("OccupancyPercent"), "vgprs": rec.get("kernel_resources", {}).get("VGPR_Count"),
+            "source": f"profiles/counters_{workload}.json"}
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in keep.items() if v is not None}
+
+
+def attention_flops(cfg, lens, tree_parents=None) -> int:
+    """Useful flops of a call: a multiply and an add for QK and again for P.V
+    over every visible (query head, row, token) triple, 4 * d each. A chain of
+    drafted tokens sees the context and the drafts up to itself; a tree node
+    sees the context and its own ancestors (parent index -1: the context)."""
+    total = 0
+    for b, L in enumerate(lens.astype(np.int64)):
+        for i in range(cfg.q_len):
+            if tree_parents is None:
+                seen = i + 1
+            else:
+                seen, p = 1, int(tree_parents[b][i])
+                while p >= 0:
+                    seen, p = seen + 1, int(tree_parents[b][p])
+            total += 4 * cfg.num_q_heads * cfg.head_dim * int(L - cfg.q_len + seen)
+    return total
+
+
 def read_probe(gib: int = 4, reps: int = 10):
     """Practical HBM read ceiling: the library's read probe over a `gib` GiB
     buffer read once per call as 8 KiB blocks in a seeded random order (the
@@ -352,10 +432,17 @@ def main():
                     help="measure the device's read ceiling (8 KiB blocks in random order) and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs and exit")
-    ap.add_argument("--bench-json", help="with --pmc-summary: a bench line of the workload (data-dependent bytes)")
+    ap.add_argument("--bench-json", help="with --pmc-summary: a bench line of the workload (data-dependent bytes); "
+                                         "with --counter-summary: the launch time and kernel name")
+    ap.add_argument("--counter-summary", nargs="+", metavar="RUN_DIR",
+                    help="write profiles/counters_<workload>.json from rocprofv3 --pmc runs (utilisation "
+                         "counters) and a --bench-json line, and exit")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args.workload, *args.pmc_summary, bench_json=args.bench_json)
+        return
+    if args.counter_summary:
+        counter_summary(args.workload, args.counter_summary, args.bench_json)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -458,6 +545,7 @@ def main():
         "tokens_per_s": round(tokens, 1),
         "tokens_per_s_80_layers": round(tokens / 80, 2),
         "algorithmic_bytes": nbytes,
+        "flops": attention_flops(cfg, w.lens, w.tree_parents),
         "roofline": {
             "bound": "hbm",
             "kernel": kernel,
@@ -473,6 +561,9 @@ def main():
         },
         "wall_s_timed_region": round(t_wall, 4),
     }
+    counters = committed_counters(cfg.name, kernel)
+    if counters is not None:
+        result["roofline"]["counters"] = counters
     if args.copy_probe:
         result["copy_probe"] = copy_probe()
     if not args.no_cpu_baseline:

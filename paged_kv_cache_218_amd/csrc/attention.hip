@@ -293,8 +293,6 @@ template <int D>
 struct StepBuf {
   u32x4 k[2][D / 32];  // two 16-token K tiles, D/32 k-steps each
   u32x4 v[D / 16];     // V^T head-dim tiles
-  int tb;              // first token of the step
-  bool ok;             // block ids in range
 };
 
 // FP8 pools: 16 K codes per lane per 64-element slab (two MFMA k-steps), 8 V
@@ -342,6 +340,15 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
   const int lane = threadIdx.x % 64;
   const int n = lane & 15, j = lane >> 4;
   const int R = a.group * a.q_len;
+  // The segment and the step range are the same in every lane of the wave
+  // (they come from LDS, so the compiler cannot see it): held in scalar
+  // registers, the table entries become scalar loads, which never wait on
+  // the K/V loads in flight.
+  b = __builtin_amdgcn_readfirstlane(b);
+  g = __builtin_amdgcn_readfirstlane(g);
+  L = __builtin_amdgcn_readfirstlane(L);
+  first = __builtin_amdgcn_readfirstlane(first);
+  end = __builtin_amdgcn_readfirstlane(end);
   if (first >= end) return;
 
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
@@ -543,89 +550,84 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
       compute_step8(buf);
     }
   } else {
-  const int64_t head_stride = int64_t(BS) * D;  // elements of one (block, head) slice
-  
-    // Issue the loads of one 32-token step into a register buffer. The
-    // physical block ids are scalar (wave-uniform) loads from the table.
-    auto load_step = [&](StepBuf<D>& buf, int step) {
-      const int tb = kStep * step;
-      buf.tb = tb;
-      const int blk0 = table[tb / BS];
-      const bool have1 = BS == 32 || tb + 16 < L;
-      const int blk1 = (BS == 16 && have1) ? table[tb / BS + 1] : blk0;
-      buf.ok = blk0 >= 0 && blk0 < a.nb && blk1 >= 0 && blk1 < a.nb;
-      const int64_t o0 = buf.ok ? (int64_t(blk0) * a.hkv + g) * head_stride : 0;
-      const int64_t o1 = buf.ok ? (int64_t(blk1) * a.hkv + g) * head_stride : 0;
-      // K tiles: A operand, token of row n in tile i. K slab ks holds head-dim
-      // elements 32ks..32ks+31 of the block's tokens back to back (64 B each),
-      // so one load instruction reads tokens {0-3, 8-11, 16-19, 24-27} (tile 0)
-      // or {4-7, ...} (tile 1) of slab ks: four runs of 256 contiguous bytes.
-  #pragma unroll
+    const int64_t head_stride = int64_t(BS) * D;  // elements of one (block, head) slice
+    // Where one 32-token step's K and V live (wave-uniform; the block ids are
+    // scalar loads from the table).
+    struct StepLoc {
+      int tb;          // first token of the step
+      int64_t o0, o1;  // offsets of the (block, head) slices of tokens 0-15 and 16-31
+      bool ok;         // block ids in range
+    };
+    // The table is never written during a launch: read through the constant
+    // address space, its entries are scalar loads.
+    const __attribute__((address_space(4))) int32_t* ctable =
+        (const __attribute__((address_space(4))) int32_t*)(table);
+    auto locate = [&](int step) {
+      StepLoc s;
+      s.tb = kStep * step;
+      const int blk0 = ctable[s.tb / BS];
+      const bool have1 = BS == 32 || s.tb + 16 < L;  // block size 16: tokens 16-31 exist
+      const int blk1 = (BS == 16 && have1) ? ctable[s.tb / BS + 1] : blk0;
+      s.ok = blk0 >= 0 && blk0 < a.nb && blk1 >= 0 && blk1 < a.nb;
+      s.o0 = s.ok ? (int64_t(blk0) * a.hkv + g) * head_stride : 0;
+      s.o1 = s.ok ? (int64_t(blk1) * a.hkv + g) * head_stride : 0;
+      return s;
+    };
+    // K tiles: A operand, token of row n in tile i. K slab ks holds head-dim
+    // elements 32ks..32ks+31 of the block's tokens back to back (64 B each),
+    // so one load instruction reads tokens {0-3, 8-11, 16-19, 24-27} (tile 0)
+    // or {4-7, ...} (tile 1) of slab ks: four runs of 256 contiguous bytes.
+    // The loads are unconditional (a branch per load would leave the compiler
+    // unable to count them and make it wait for every load in flight), and
+    // always in bounds: a bad block id reads slice 0 and the step is not
+    // computed; a missing second block (block size 16, tokens 16-31 past the
+    // context) re-reads the first, whose tokens are then masked: scores by a
+    // select, V entries zeroed before P.V.
+    auto load_k = [&](StepBuf<D>& buf, const StepLoc& s) {
+#pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int tok = 8 * (n >> 2) + 4 * i + (n & 3);
         const bool second = BS == 16 && tok >= 16;
-        const uint16_t* row = kp + (second ? o1 : o0) + (tok & (BS - 1)) * 32 + 8 * j;
-        const bool ok = buf.ok && (!second || have1);
-  #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          u32x4 v = {0, 0, 0, 0};
-          if (ok) v = load16<STREAM>(row + ks * (BS * 32));
-          buf.k[i][ks] = v;
-        }
-      }
-      // V^T slices: A operand of PV, head-dim row 16*dt + n, tokens 8j..8j+7
-      {
-        const bool second = BS == 16 && j >= 2;
-        const uint16_t* base = vp + (second ? o1 : o0) + (BS == 32 ? 8 * j : 8 * (j & 1)) + n * BS;
-        const bool ok = buf.ok && (!second || have1);
-  #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          u32x4 v = {0, 0, 0, 0};
-          if (ok) v = load16<STREAM>(base + 16 * dt * BS);
-          buf.v[dt] = v;
-        }
+        const uint16_t* row = kp + (second ? s.o1 : s.o0) + (tok & (BS - 1)) * 32 + 8 * j;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) buf.k[i][ks] = load16<STREAM>(row + ks * (BS * 32));
       }
     };
-  
-    // Scores, online softmax and P.V of one loaded step.
-    auto compute_step = [&](StepBuf<D>& buf) {
-      const int tb = buf.tb;
-      if (!buf.ok) {
-        st.poisoned = true;
-        return;
-      }
-      // tail step: zero V entries past the context so 0 * NaN never reaches the sum
-      if (tb + kStep > L) {
-        const int valid = min(max(L - (tb + 8 * j), 0), 8);  // tokens of this lane's 8 still valid
-  #pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {
-          const uint32_t keep = (2 * w4 + 1 < valid) ? 0xffffffffu : (2 * w4 < valid ? 0x0000ffffu : 0u);
-  #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) buf.v[dt][w4] &= keep;
-        }
-      }
-  #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 sc[2];
-  #pragma unroll
+    // V^T slices: A operand of PV, head-dim row 16*dt + n, tokens 8j..8j+7
+    auto load_v = [&](StepBuf<D>& buf, const StepLoc& s) {
+      const bool second = BS == 16 && j >= 2;
+      const uint16_t* base = vp + (second ? s.o1 : s.o0) + (BS == 32 ? 8 * j : 8 * (j & 1)) + n * BS;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) buf.v[dt] = load16<STREAM>(base + 16 * dt * BS);
+    };
+
+    // Scores of every row tile (the step's last use of K), then the online
+    // softmax: leaves the bf16 probabilities and the rescale factors for P.V.
+    auto scores = [&](const StepBuf<D>& buf, int tb, u32x4 (&pop)[NT], float (&alpha)[NT]) {
+      f32x4 sc[NT][2];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
         for (int i = 0; i < 2; ++i) {
-          sc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
+          sc[nt][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            sc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf.k[i][ks]),
-                                                             __builtin_bit_cast(bf16x8, qop[nt][ks]),
-                                                             sc[i], 0, 0, 0);
+            sc[nt][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf.k[i][ks]),
+                                                                 __builtin_bit_cast(bf16x8, qop[nt][ks]),
+                                                                 sc[nt][i], 0, 0, 0);
         }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
         // mask and scale; e = 4*i + r is token tb + 8j + e
         float s2[8];
         float mx = -INFINITY;
         const uint32_t tbits = TREE ? tree_bits(tb, nt) : 0u;
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 2; ++i)
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 4; ++r) {
             const bool vis = visible(tb + 8 * j + 4 * i + r, nt, tbits, 4 * i + r);
-            const float v = vis ? sc[i][r] * a.scale_log2 : -INFINITY;
+            const float v = vis ? sc[nt][i][r] * a.scale_log2 : -INFINITY;
             s2[4 * i + r] = v;
             mx = fmaxf(mx, v);
           }
@@ -633,11 +635,11 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(st.m[nt], mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(st.m[nt] - m_use);
+        alpha[nt] = fast_exp2(st.m[nt] - m_use);
         st.m[nt] = m_new;
         uint32_t pk[4];
         float psum = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int w4 = 0; w4 < 4; ++w4) {
           const float p0 = fast_exp2(s2[2 * w4] - m_use);
           const float p1 = fast_exp2(s2[2 * w4 + 1] - m_use);
@@ -646,26 +648,65 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
           // the sum uses the rounded weights, so the output stays a convex combination
           psum += __uint_as_float(packed << 16) + __uint_as_float(packed & 0xffff0000u);
         }
-        st.l[nt] = st.l[nt] * alpha + psum;
-        const u32x4 pop = {pk[0], pk[1], pk[2], pk[3]};
-  #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          st.acc[nt][dt] *= alpha;
-          st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf.v[dt]),
-                                                                   __builtin_bit_cast(bf16x8, pop),
+        st.l[nt] = st.l[nt] * alpha[nt] + psum;
+        pop[nt] = (u32x4){pk[0], pk[1], pk[2], pk[3]};
+      }
+    };
+
+    // P.V of one step (the step's only use of V).
+    auto accumulate = [&](StepBuf<D>& buf, int tb, const u32x4 (&pop)[NT], const float (&alpha)[NT]) {
+      // zero V entries past the context so 0 * NaN never reaches the sum (a
+      // select on every step rather than a branch on the tail step)
+      const int valid = min(max(L - (tb + 8 * j), 0), 8);  // tokens of this lane's 8 still valid
+      uint32_t keep[4];
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4)
+        keep[w4] = (2 * w4 + 1 < valid) ? 0xffffffffu : (2 * w4 < valid ? 0x0000ffffu : 0u);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x4 vm = {buf.v[dt][0] & keep[0], buf.v[dt][1] & keep[1], buf.v[dt][2] & keep[2],
+                          buf.v[dt][3] & keep[3]};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          st.acc[nt][dt] *= alpha[nt];
+          st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vm),
+                                                                   __builtin_bit_cast(bf16x8, pop[nt]),
                                                                    st.acc[nt][dt], 0, 0, 0);
         }
       }
     };
-  
-    // One step buffer per wave: the other waves on the SIMD (three per SIMD
-    // fit) hide this wave's load latency. (A two-buffer ping-pong was measured
-    // no faster: the extra registers cost a wave per SIMD.)
+
+    // One K and one V buffer per wave, each refilled with the next step's
+    // loads as soon as the current step has consumed it: the next K goes out
+    // after the scores, the next V after P.V, so the wave keeps about a
+    // step's bytes in flight while it computes, in the registers of a single
+    // buffer. (Loads complete in issue order, so the wait for K before the
+    // scores leaves V in flight, and the wait for V before P.V leaves the
+    // next K in flight.)
+    // The loop body is straight-line (the last step is peeled off, and a
+    // step with a bad block id is computed on slice 0 and only marks the
+    // wave poisoned: its rows are written as NaN), so the compiler can count
+    // the loads in flight exactly.
     StepBuf<D> buf;
-    for (int s = first; s < end; s = next_step(s)) {
-      load_step(buf, s);
-      compute_step(buf);
+    StepLoc cur = locate(first);
+    load_k(buf, cur);
+    load_v(buf, cur);
+    for (int sn = next_step(first); sn < end; sn = next_step(sn)) {
+      const StepLoc nxt = locate(sn);
+      u32x4 pop[NT];
+      float alpha[NT];
+      scores(buf, cur.tb, pop, alpha);
+      load_k(buf, nxt);
+      accumulate(buf, cur.tb, pop, alpha);
+      load_v(buf, nxt);
+      st.poisoned |= !cur.ok;
+      cur = nxt;
     }
+    u32x4 pop[NT];
+    float alpha[NT];
+    scores(buf, cur.tb, pop, alpha);
+    accumulate(buf, cur.tb, pop, alpha);
+    st.poisoned |= !cur.ok;
   }
 }
 
