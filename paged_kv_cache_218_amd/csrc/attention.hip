@@ -303,8 +303,6 @@ struct StepBuf8 {
   u32x4 k[2][D / 64];
   u32x2 v[D / 16];
   f32x4 ks[2], vs[2];
-  int tb;
-  bool ok;
 };
 
 // Online-softmax state of one wavefront: lane (n, j) holds row 16*nt + n,
@@ -401,56 +399,77 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     else return tok < L && tok <= lim[nt];
   };
 
+  // Where one 32-token step's K and V live (wave-uniform). The table is never
+  // written during a launch: read through the constant address space, its
+  // entries are scalar loads, which never wait on the K/V loads in flight.
+  struct StepLoc {
+    int tb;          // first token of the step
+    int64_t s0, s1;  // (block, head) slices of tokens 0-15 and 16-31
+    bool ok;         // block ids in range
+  };
+  const __attribute__((address_space(4))) int32_t* ctable =
+      (const __attribute__((address_space(4))) int32_t*)(table);
+  auto locate = [&](int step) {
+    StepLoc s;
+    s.tb = kStep * step;
+    const int blk0 = ctable[s.tb / BS];
+    const bool have1 = BS == 32 || s.tb + 16 < L;  // block size 16: tokens 16-31 exist
+    const int blk1 = (BS == 16 && have1) ? ctable[s.tb / BS + 1] : blk0;
+    s.ok = blk0 >= 0 && blk0 < a.nb && blk1 >= 0 && blk1 < a.nb;
+    s.s0 = s.ok ? int64_t(blk0) * a.hkv + g : 0;
+    s.s1 = s.ok ? int64_t(blk1) * a.hkv + g : 0;
+    return s;
+  };
+  // Both step loops below keep one K and one V buffer per wave and refill
+  // each with the next step's loads as soon as the current step has consumed
+  // it: the next K right after the score MFMAs, the next V during P.V. A wave
+  // thus keeps about a step's bytes in flight while it computes, in the
+  // registers of one buffer (loads complete in issue order, so waiting for K
+  // leaves V in flight and waiting for V leaves the next K in flight).
+  //
+  // The loads are unconditional (a branch per load would leave the compiler
+  // unable to count them, and it would wait for every load in flight), and
+  // always in bounds: a bad block id reads slice 0, the step is computed on
+  // it and the wave is marked poisoned (its rows are written as NaN); a
+  // missing second block (block size 16, tokens 16-31 past the context)
+  // re-reads the first, whose tokens are then masked: scores by a select, V
+  // entries zeroed before P.V. The last step is peeled off the loop, so the
+  // loop body is straight-line.
+
   if constexpr (KV8) {
     const uint8_t* __restrict__ kc = static_cast<const uint8_t*>(a.k_pool);
     const uint8_t* __restrict__ vc = static_cast<const uint8_t*>(a.v_pool);
     const int64_t slice = int64_t(BS) * D;  // bytes of one (block, head) code slice
-    auto load_step8 = [&](StepBuf8<D>& buf, int step) {
-      const int tb = kStep * step;
-      buf.tb = tb;
-      const int blk0 = table[tb / BS];
-      const bool have1 = BS == 32 || tb + 16 < L;
-      const int blk1 = (BS == 16 && have1) ? table[tb / BS + 1] : blk0;
-      buf.ok = blk0 >= 0 && blk0 < a.nb && blk1 >= 0 && blk1 < a.nb;
-      const int64_t s0 = buf.ok ? int64_t(blk0) * a.hkv + g : 0;  // slice index
-      const int64_t s1 = buf.ok ? int64_t(blk1) * a.hkv + g : 0;
+    // the lane's 8 tokens 8j..8j+7 of the step: their block and offset in it
+    const bool second8 = BS == 16 && j >= 2;
+    const int toff = BS == 32 ? 8 * j : 8 * (j & 1);
+    // K codes (same lane layout as the bf16 tiles, 16 codes per 64-element
+    // slab) and the K scales of the lane's 8 tokens
+    auto load_k8 = [&](StepBuf8<D>& buf, const StepLoc& s) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int tok = 8 * (n >> 2) + 4 * i + (n & 3);
         const bool second = BS == 16 && tok >= 16;
-        const uint8_t* row = kc + (second ? s1 : s0) * slice + (tok & (BS - 1)) * 64 + 16 * j;
-        const bool ok = buf.ok && (!second || have1);
+        const uint8_t* row = kc + (second ? s.s1 : s.s0) * slice + (tok & (BS - 1)) * 64 + 16 * j;
 #pragma unroll
-        for (int sl = 0; sl < D / 64; ++sl) {
-          u32x4 v = {0, 0, 0, 0};
-          if (ok) v = load16<STREAM>(row + sl * (BS * 64));
-          buf.k[i][sl] = v;
-        }
+        for (int sl = 0; sl < D / 64; ++sl) buf.k[i][sl] = load16<STREAM>(row + sl * (BS * 64));
       }
-      const bool second = BS == 16 && j >= 2;
-      const bool ok = buf.ok && (!second || have1);
-      const int toff = BS == 32 ? 8 * j : 8 * (j & 1);  // the lane's 8 tokens within their block
-      const int64_t sl_idx = second ? s1 : s0;
-      const uint8_t* base = vc + sl_idx * slice + toff + n * BS;
+      const int64_t si = second8 ? s.s1 : s.s0;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        u32x2 v = {0, 0};
-        if (ok) v = load8<STREAM>(base + 16 * dt * BS);
-        buf.v[dt] = v;
-      }
-      const f32x4 one = {1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        buf.ks[h] = ok ? load16f<STREAM>(a.k_scales + sl_idx * BS + toff + 4 * h) : one;
-        buf.vs[h] = ok ? load16f<STREAM>(a.v_scales + sl_idx * BS + toff + 4 * h) : one;
-      }
+      for (int h = 0; h < 2; ++h) buf.ks[h] = load16f<STREAM>(a.k_scales + si * BS + toff + 4 * h);
     };
-    auto compute_step8 = [&](StepBuf8<D>& buf) {
-      const int tb = buf.tb;
-      if (!buf.ok) {
-        st.poisoned = true;
-        return;
-      }
+    // V^T codes (8 per lane per head-dim tile) and the V scales of the lane's 8 tokens
+    auto load_v8 = [&](StepBuf8<D>& buf, const StepLoc& s) {
+      const int64_t si = second8 ? s.s1 : s.s0;
+      const uint8_t* base = vc + si * slice + toff + n * BS;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) buf.v[dt] = load8<STREAM>(base + 16 * dt * BS);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) buf.vs[h] = load16f<STREAM>(a.v_scales + si * BS + toff + 4 * h);
+    };
+    // Scores of every row tile, each times its token's K scale (exact: the
+    // scale multiplies the dot product): the step's only use of K.
+    auto qk8 = [&](const StepBuf8<D>& buf, f32x4 (&sc)[NT][2]) {
       // codes -> bf16 (exact); K: slab sl gives k-steps 2sl (codes 0-7) and 2sl+1 (8-15)
       u32x4 kop[2][KS];
 #pragma unroll
@@ -463,35 +482,29 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
             kop[i][2 * sl + hh] = (u32x4){fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
                                           fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1)};
           }
-      u32x4 vop[DT];
-      const int valid = min(max(L - (tb + 8 * j), 0), 8);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const uint32_t w0 = buf.v[dt][0], w1 = buf.v[dt][1];
-        vop[dt] = (u32x4){fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
-                          fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1)};
-      }
-      if (tb + kStep > L) {  // tail: tokens past the context hold the NaN code
-#pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {
-          const uint32_t keep = (2 * w4 + 1 < valid) ? 0xffffffffu : (2 * w4 < valid ? 0x0000ffffu : 0u);
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) vop[dt][w4] &= keep;
-        }
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 sc[2];
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          sc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          sc[nt][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            sc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[i][ks]),
-                                                             __builtin_bit_cast(bf16x8, qop[nt][ks]),
-                                                             sc[i], 0, 0, 0);
+            sc[nt][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[i][ks]),
+                                                                 __builtin_bit_cast(bf16x8, qop[nt][ks]),
+                                                                 sc[nt][i], 0, 0, 0);
+          // e = 4i + r is token tb + 8j + e
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[nt][i][r] *= buf.ks[i][r];
         }
-        // each token's K scale multiplies its score; e = 4i + r is token tb + 8j + e
+    };
+    // Online softmax. Each token's V scale multiplies its weight in P.V (not
+    // in the row sum). The scaled weight w is not a bf16 number, so it enters
+    // P.V as w_hi + w_lo, two bf16 parts (residual ~2^-17 relative): one
+    // dominant token would otherwise carry w's 2^-9 rounding into the row.
+    auto softmax8 = [&](const f32x4 (&sc)[NT][2], const StepBuf8<D>& buf, int tb, u32x4 (&pop_hi)[NT],
+                        u32x4 (&pop_lo)[NT], float (&alpha)[NT]) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
         float s2[8];
         bool vis[8];
         float mx = -INFINITY;
@@ -502,7 +515,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
           for (int r = 0; r < 4; ++r) {
             const int e = 4 * i + r;
             vis[e] = visible(tb + 8 * j + e, nt, tbits, e);
-            const float v = vis[e] ? sc[i][r] * buf.ks[i][r] * a.scale_log2 : -INFINITY;
+            const float v = vis[e] ? sc[nt][i][r] * a.scale_log2 : -INFINITY;
             s2[e] = v;
             mx = fmaxf(mx, v);
           }
@@ -510,12 +523,8 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(st.m[nt], mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(st.m[nt] - m_use);
+        alpha[nt] = fast_exp2(st.m[nt] - m_use);
         st.m[nt] = m_new;
-        // Each token's V scale multiplies its weight in P.V (not in the row
-        // sum). The scaled weight w is not a bf16 number, so it enters P.V as
-        // w_hi + w_lo, two bf16 parts (residual ~2^-17 relative): one
-        // dominant token would otherwise carry w's 2^-9 rounding into the row.
         uint32_t pk_hi[4], pk_lo[4];
         float psum = 0.f;
 #pragma unroll
@@ -529,66 +538,75 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
           pk_hi[w4] = hi;
           pk_lo[w4] = pack_bf16x2(q0 - __uint_as_float(hi << 16), q1 - __uint_as_float(hi & 0xffff0000u));
         }
-        st.l[nt] = st.l[nt] * alpha + psum;
-        const u32x4 pop_hi = {pk_hi[0], pk_hi[1], pk_hi[2], pk_hi[3]};
-        const u32x4 pop_lo = {pk_lo[0], pk_lo[1], pk_lo[2], pk_lo[3]};
+        st.l[nt] = st.l[nt] * alpha[nt] + psum;
+        pop_hi[nt] = (u32x4){pk_hi[0], pk_hi[1], pk_hi[2], pk_hi[3]};
+        pop_lo[nt] = (u32x4){pk_lo[0], pk_lo[1], pk_lo[2], pk_lo[3]};
+      }
+    };
+    // P.V of one step (the step's only use of the V codes).
+    auto accumulate8 = [&](const StepBuf8<D>& buf, int tb, const u32x4 (&pop_hi)[NT],
+                           const u32x4 (&pop_lo)[NT], const float (&alpha)[NT]) {
+      // tokens past the context hold the NaN code: zeroed on every step (a select, no branch)
+      const int valid = min(max(L - (tb + 8 * j), 0), 8);
+      uint32_t keep[4];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          st.acc[nt][dt] *= alpha;
-          st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[dt]),
-                                                                   __builtin_bit_cast(bf16x8, pop_hi),
+      for (int w4 = 0; w4 < 4; ++w4)
+        keep[w4] = (2 * w4 + 1 < valid) ? 0xffffffffu : (2 * w4 < valid ? 0x0000ffffu : 0u);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint32_t w0 = buf.v[dt][0], w1 = buf.v[dt][1];
+        const u32x4 vop = {fp8x2_to_bf16x2<false>(w0) & keep[0], fp8x2_to_bf16x2<true>(w0) & keep[1],
+                           fp8x2_to_bf16x2<false>(w1) & keep[2], fp8x2_to_bf16x2<true>(w1) & keep[3]};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          st.acc[nt][dt] *= alpha[nt];
+          st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop),
+                                                                   __builtin_bit_cast(bf16x8, pop_hi[nt]),
                                                                    st.acc[nt][dt], 0, 0, 0);
-          st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[dt]),
-                                                                   __builtin_bit_cast(bf16x8, pop_lo),
+          st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop),
+                                                                   __builtin_bit_cast(bf16x8, pop_lo[nt]),
                                                                    st.acc[nt][dt], 0, 0, 0);
         }
       }
     };
     StepBuf8<D> buf;
-    for (int s = first; s < end; s = next_step(s)) {
-      load_step8(buf, s);
-      compute_step8(buf);
+    StepLoc cur = locate(first);
+    load_k8(buf, cur);
+    load_v8(buf, cur);
+    for (int sn = next_step(first); sn < end; sn = next_step(sn)) {
+      const StepLoc nxt = locate(sn);
+      f32x4 sc[NT][2];
+      u32x4 hi[NT], lo[NT];
+      float alpha[NT];
+      qk8(buf, sc);
+      __builtin_amdgcn_sched_barrier(0);
+      load_k8(buf, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax8(sc, buf, cur.tb, hi, lo, alpha);
+      accumulate8(buf, cur.tb, hi, lo, alpha);
+      load_v8(buf, nxt);
+      st.poisoned |= !cur.ok;
+      cur = nxt;
     }
+    f32x4 sc[NT][2];
+    u32x4 hi[NT], lo[NT];
+    float alpha[NT];
+    qk8(buf, sc);
+    softmax8(sc, buf, cur.tb, hi, lo, alpha);
+    accumulate8(buf, cur.tb, hi, lo, alpha);
+    st.poisoned |= !cur.ok;
   } else {
     const int64_t head_stride = int64_t(BS) * D;  // elements of one (block, head) slice
-    // Where one 32-token step's K and V live (wave-uniform; the block ids are
-    // scalar loads from the table).
-    struct StepLoc {
-      int tb;          // first token of the step
-      int64_t o0, o1;  // offsets of the (block, head) slices of tokens 0-15 and 16-31
-      bool ok;         // block ids in range
-    };
-    // The table is never written during a launch: read through the constant
-    // address space, its entries are scalar loads.
-    const __attribute__((address_space(4))) int32_t* ctable =
-        (const __attribute__((address_space(4))) int32_t*)(table);
-    auto locate = [&](int step) {
-      StepLoc s;
-      s.tb = kStep * step;
-      const int blk0 = ctable[s.tb / BS];
-      const bool have1 = BS == 32 || s.tb + 16 < L;  // block size 16: tokens 16-31 exist
-      const int blk1 = (BS == 16 && have1) ? ctable[s.tb / BS + 1] : blk0;
-      s.ok = blk0 >= 0 && blk0 < a.nb && blk1 >= 0 && blk1 < a.nb;
-      s.o0 = s.ok ? (int64_t(blk0) * a.hkv + g) * head_stride : 0;
-      s.o1 = s.ok ? (int64_t(blk1) * a.hkv + g) * head_stride : 0;
-      return s;
-    };
     // K tiles: A operand, token of row n in tile i. K slab ks holds head-dim
     // elements 32ks..32ks+31 of the block's tokens back to back (64 B each),
     // so one load instruction reads tokens {0-3, 8-11, 16-19, 24-27} (tile 0)
     // or {4-7, ...} (tile 1) of slab ks: four runs of 256 contiguous bytes.
-    // The loads are unconditional (a branch per load would leave the compiler
-    // unable to count them and make it wait for every load in flight), and
-    // always in bounds: a bad block id reads slice 0 and the step is not
-    // computed; a missing second block (block size 16, tokens 16-31 past the
-    // context) re-reads the first, whose tokens are then masked: scores by a
-    // select, V entries zeroed before P.V.
     auto load_k = [&](StepBuf<D>& buf, const StepLoc& s) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int tok = 8 * (n >> 2) + 4 * i + (n & 3);
         const bool second = BS == 16 && tok >= 16;
-        const uint16_t* row = kp + (second ? s.o1 : s.o0) + (tok & (BS - 1)) * 32 + 8 * j;
+        const uint16_t* row = kp + (second ? s.s1 : s.s0) * head_stride + (tok & (BS - 1)) * 32 + 8 * j;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) buf.k[i][ks] = load16<STREAM>(row + ks * (BS * 32));
       }
@@ -596,15 +614,13 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     // V^T slices: A operand of PV, head-dim row 16*dt + n, tokens 8j..8j+7
     auto load_v = [&](StepBuf<D>& buf, const StepLoc& s) {
       const bool second = BS == 16 && j >= 2;
-      const uint16_t* base = vp + (second ? s.o1 : s.o0) + (BS == 32 ? 8 * j : 8 * (j & 1)) + n * BS;
+      const uint16_t* base = vp + (second ? s.s1 : s.s0) * head_stride + (BS == 32 ? 8 * j : 8 * (j & 1)) + n * BS;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) buf.v[dt] = load16<STREAM>(base + 16 * dt * BS);
     };
 
-    // Scores of every row tile (the step's last use of K), then the online
-    // softmax: leaves the bf16 probabilities and the rescale factors for P.V.
-    auto scores = [&](const StepBuf<D>& buf, int tb, u32x4 (&pop)[NT], float (&alpha)[NT]) {
-      f32x4 sc[NT][2];
+    // Scores of every row tile: the step's only use of K.
+    auto qk = [&](const StepBuf<D>& buf, f32x4 (&sc)[NT][2]) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -616,6 +632,10 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
                                                                  __builtin_bit_cast(bf16x8, qop[nt][ks]),
                                                                  sc[nt][i], 0, 0, 0);
         }
+    };
+    // Online softmax of the scores: leaves the bf16 probabilities and the
+    // rescale factors for P.V.
+    auto softmax = [&](const f32x4 (&sc)[NT][2], int tb, u32x4 (&pop)[NT], float (&alpha)[NT]) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         // mask and scale; e = 4*i + r is token tb + 8j + e
@@ -683,28 +703,31 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     // buffer. (Loads complete in issue order, so the wait for K before the
     // scores leaves V in flight, and the wait for V before P.V leaves the
     // next K in flight.)
-    // The loop body is straight-line (the last step is peeled off, and a
-    // step with a bad block id is computed on slice 0 and only marks the
-    // wave poisoned: its rows are written as NaN), so the compiler can count
-    // the loads in flight exactly.
     StepBuf<D> buf;
     StepLoc cur = locate(first);
     load_k(buf, cur);
     load_v(buf, cur);
     for (int sn = next_step(first); sn < end; sn = next_step(sn)) {
       const StepLoc nxt = locate(sn);
+      f32x4 sc[NT][2];
       u32x4 pop[NT];
       float alpha[NT];
-      scores(buf, cur.tb, pop, alpha);
+      qk(buf, sc);
+      // the next K loads go out right after the score MFMAs, before the softmax
+      __builtin_amdgcn_sched_barrier(0);
       load_k(buf, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax(sc, cur.tb, pop, alpha);
       accumulate(buf, cur.tb, pop, alpha);
       load_v(buf, nxt);
       st.poisoned |= !cur.ok;
       cur = nxt;
     }
+    f32x4 sc[NT][2];
     u32x4 pop[NT];
     float alpha[NT];
-    scores(buf, cur.tb, pop, alpha);
+    qk(buf, sc);
+    softmax(sc, cur.tb, pop, alpha);
     accumulate(buf, cur.tb, pop, alpha);
     st.poisoned |= !cur.ok;
   }
