@@ -13,7 +13,7 @@ from tests.gpu_util import assert_close, oracle_rows, out_to_f64, run_gpu  # noq
 
 SAMPLE = {"tiny_f32": None, "llama3_8b_decode": [0, 17, 63], "llama3_70b_decode": [0, 41],
           "prefix_verify": [0, 64, 127], "long_ctx_split": [3], "llama3_70b_decode_fp8": [0, 63],
-          "tree_verify": [0, 77, 127]}
+          "tree_verify": [0, 77, 127], "prefix_verify_fp8": [0, 127]}
 
 
 def model_tables(w):

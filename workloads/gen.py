@@ -107,6 +107,12 @@ CONFIGS = {
         Config("llama3_70b_decode_fp8", 2, batch=64, q_len=1, num_q_heads=64,
                num_kv_heads=8, head_dim=128, block_size=32, dtype="bf16",
                len_const=8192, kv_dtype="fp8"),
+        # prefix-shared verification over an FP8 KV cache (same seeds and
+        # values as prefix_verify)
+        Config("prefix_verify_fp8", 3, batch=128, q_len=5, num_q_heads=32,
+               num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
+               prefix_len=512, len_lo=512, len_hi=3584, pool_slack=1.25,
+               kv_dtype="fp8"),
     ]
 }
 
