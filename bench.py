@@ -215,7 +215,7 @@ def counter_summary(workload: str, run_dirs, bench_json: str):
     rec = json.loads(open(bench_json).read().strip().splitlines()[-1])
     kernel = rec["roofline"]["kernel"]
     launch_us = rec["roofline"]["launch_us"]
-    values, regs = {}, {}
+    values = {}
     for d in run_dirs:
         rows = [r for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv")))
                 if kernel in r["Kernel_Name"]]
@@ -223,12 +223,9 @@ def counter_summary(workload: str, run_dirs, bench_json: str):
             raise SystemExit(f"{d}: no {kernel} dispatches")
         for r in rows:
             values.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-            for key in ("VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "LDS_Block_Size", "Workgroup_Size"):
-                if r.get(key) not in (None, ""):
-                    regs[key] = int(float(r[key]))
     out = {"workload": workload, "kernel": kernel, "source_sha256": source_digest(),
            "launch_us": launch_us, "dispatches": {k: len(v) for k, v in values.items()},
-           "per_launch": {k: statistics.mean(v) for k, v in values.items()}, "kernel_resources": regs}
+           "per_launch": {k: statistics.mean(v) for k, v in values.items()}}
     flops = out["per_launch"].get("MfmaFlopsBF16")
     if flops is not None:
         tflops = flops / (launch_us * 1e-6) / 1e12
@@ -256,8 +253,7 @@ def committed_counters(workload: str, kernel: str):
     pl = rec["per_launch"]
     keep = {"mfma_util_pct": pl.get("MfmaUtil"), "mfma_bf16_tflops": rec.get("mfma_bf16_tflops"),
             "mfma_bf16_frac_of_peak": rec.get("mfma_bf16_frac_of_peak"), "valu_busy_pct": pl.get("VALUBusy"),
-            "occupancy_pct": pl.get("OccupancyPercent"), "vgprs": rec.get("kernel_resources", {}).get("VGPR_Count"),
-            "source": f"profiles/counters_{workload}.json"}
+            "occupancy_pct": pl.get("OccupancyPercent"), "source": f"profiles/counters_{workload}.json"}
     return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in keep.items() if v is not None}
 
 
