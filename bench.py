@@ -96,7 +96,7 @@ def kernel_name(cfg, plan, desc) -> str:
     if plan.path == 1:
         t = "float" if cfg.dtype == "f32" else "unsigned short"
         return f"valu_attn<{t}, {cfg.head_dim}, {cfg.block_size}>"
-    base = "mfma_attn_balanced" if plan.schedule == 1 else "mfma_attn"
+    base = {0: "mfma_attn", 1: "mfma_attn_balanced", 2: "mfma_attn_wave"}[plan.schedule]
     nt = plan.tiles_per_wave
     stream = "false" if desc.kv_shared else "true"
     kv8 = "true" if desc.kv_format else "false"
@@ -533,7 +533,7 @@ def main():
             "kv_storage": "fp8_e4m3+scales" if cfg.kv_dtype == "fp8" else cfg.dtype,
             "drafted_tokens": f"tree ({cfg.tree})" if cfg.tree else ("chain" if cfg.q_len > 1 else "none"),
             "path": path_name, "partition_tokens": plan.partition_tokens,
-            "schedule": {0: "partitions", 1: "balanced"}[plan.schedule], "kv_shared": int(desc.kv_shared),
+            "schedule": {0: "partitions", 1: "balanced", 2: "partitions_wave"}[plan.schedule], "kv_shared": int(desc.kv_shared),
             "partitions": plan.num_partitions, "waves_per_group": plan.waves_per_group,
             "grid": plan.grid, "merge_grid": plan.merge_grid, "tiles_per_wave": plan.tiles_per_wave,
         },

@@ -99,8 +99,16 @@ enum { PA_PATH_AUTO = 0, PA_PATH_VALU = 1, PA_PATH_MFMA = 2 };
  * BALANCED: the grid holds as many workgroups as the GPU runs at once and
  *   each takes an equal share of all (sequence, KV head, 32-token step) work
  *   items; a sequence split between workgroups is merged by the workgroup
- *   that finishes its last share (one kernel, no second launch). */
-enum { PA_SCHED_PARTITIONS = 0, PA_SCHED_BALANCED = 1 };
+ *   that finishes its last share (one kernel, no second launch).
+ * PARTITIONS_WAVE: fixed-length partitions as PARTITIONS, one wavefront per
+ *   (sequence, KV head, partition), each writing its partial from registers;
+ *   chosen instead of PARTITIONS on the MFMA path when the partitions alone
+ *   fill every wave slot of the device. The same merge kernel follows.
+ * Split-KV on one GPU as on the pages: attention local to each partition of
+ * the sequence, then a reduction of the partitions' results ("Mở rộng Quy mô
+ * và Triển khai", "Song song hóa Chuỗi"; the reduction is the log-sum-exp
+ * merge). */
+enum { PA_SCHED_PARTITIONS = 0, PA_SCHED_BALANCED = 1, PA_SCHED_PARTITIONS_WAVE = 2 };
 
 /* Largest tree of drafted tokens pa_attention_tree takes: one 32-bit
  * visibility mask per node. */
@@ -248,9 +256,10 @@ typedef struct pa_attn_desc {
 /* What pa_attention launches for a descriptor (for tests and profiling). */
 typedef struct pa_attn_plan {
   int32_t path;               /* PA_PATH_VALU or PA_PATH_MFMA */
-  int32_t schedule;           /* PA_SCHED_PARTITIONS or PA_SCHED_BALANCED */
-  int32_t partition_tokens;   /* PARTITIONS: tokens per partition (0 for BALANCED) */
-  int32_t num_partitions;     /* PARTITIONS: partitions per sequence (1 = no merge pass) */
+  int32_t schedule;           /* PA_SCHED_PARTITIONS, PA_SCHED_BALANCED or
+                                 PA_SCHED_PARTITIONS_WAVE */
+  int32_t partition_tokens;   /* PARTITIONS*: tokens per partition (0 for BALANCED) */
+  int32_t num_partitions;     /* PARTITIONS*: partitions per sequence (1 = no merge pass) */
   int32_t waves_per_group;    /* wavefronts per workgroup of the main kernel */
   int32_t grid;               /* workgroups of the main kernel; BALANCED: the resident
                                  capacity of the current device for that kernel (an
@@ -280,8 +289,9 @@ size_t pa_attention_workspace_size(const pa_attn_desc* desc, int32_t q_len);
  *                drafted tokens: row i attends to positions 0..L_b-q_len+i)
  *   scale        multiplies q.k (1/sqrt(d) for standard attention)
  *   out          device [B][q_len][H_q][d], same dtype as q
- *   workspace    device, >= pa_attention_workspace_size bytes (may be NULL
- *                when that is 0); holds split-KV partials, no hidden allocation.
+ *   workspace    device, >= pa_attention_workspace_size bytes, 16-byte aligned
+ *                (may be NULL when that size is 0); holds split-KV partials, no
+ *                hidden allocation.
  *                With the BALANCED schedule its first bytes are arrival
  *                counters: the workspace must be zero-filled before its first
  *                use, and every completed call leaves them zero again. Calls

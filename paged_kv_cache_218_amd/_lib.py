@@ -14,7 +14,7 @@ PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_NO_FREE_BLOCK, PA_ERR_BAD_
 PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3 = 0, 1, 2
 PA_KV_SAME, PA_KV_FP8_E4M3 = 0, 1
 PA_PATH_AUTO, PA_PATH_VALU, PA_PATH_MFMA = 0, 1, 2
-PA_SCHED_PARTITIONS, PA_SCHED_BALANCED = 0, 1
+PA_SCHED_PARTITIONS, PA_SCHED_BALANCED, PA_SCHED_PARTITIONS_WAVE = 0, 1, 2
 PA_TREE_MAX_NODES = 32
 
 i32, i64, vp, f32, sz = C.c_int32, C.c_int64, C.c_void_p, C.c_float, C.c_size_t

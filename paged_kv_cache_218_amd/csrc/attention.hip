@@ -804,6 +804,67 @@ __global__ __launch_bounds__(256, 2) void mfma_attn(AttnArgs a) {
   merge_and_store<uint16_t, D>(a, t, R, R, W, smem, smem + W * R, smem + 2 * W * R, bad);
 }
 
+// Fixed partitions, one wavefront per partition (chosen when the partitions
+// fill the device on their own): wave w of workgroup k takes partition
+// (k % gpw) * W + w of the (sequence, KV head) pair k / gpw, gpw =
+// ceil(parts / W). It streams the partition's steps back to back through the
+// step pipeline and writes the partition's (m, l, o = acc / l) partial, or
+// the final rows of a one-partition sequence, straight from its registers:
+// no LDS, no barrier. lse_merge combines the partials as for mfma_attn.
+template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE>
+__global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void mfma_attn_wave(AttnArgs a) {
+  const int W = blockDim.x / 64, wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int n = lane & 15, j = lane >> 4;
+  const int gpw = (a.parts + W - 1) / W;
+  const int pair = blockIdx.x / gpw;
+  const int part = (blockIdx.x % gpw) * W + wave;
+  if (part >= a.parts) return;
+  const int g = pair % a.hkv, b = pair / a.hkv;
+  const int L = a.lens[b];
+  const int R = a.group * a.q_len;
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  if (L < a.q_len || L > a.max_ctx) {  // NaN rows: here for one partition, else by the merge kernel
+    if (part == 0 && a.parts == 1)
+      for (int e = lane; e < R * D; e += 64)
+        store_f<uint16_t>(out + int64_t(out_row(a, b, g, e / D)) * D + e % D, NAN);
+    return;
+  }
+  const int t0 = part * a.part_tokens;
+  if (t0 >= L) return;  // past the sequence: the merge kernel reads only its partitions
+  const int t1 = min(t0 + a.part_tokens, L);
+  WaveState<D, NT> st;
+  wave_state_init(st);
+  mfma_wave_steps<D, BS, NT, STREAM, KV8, TREE>(a, b, g, L, t0 / kStep, (t1 + kStep - 1) / kStep, st,
+                                                [](int s) { return s + 1; });
+  const bool final_rows = L <= a.part_tokens;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float l = st.l[nt] + __shfl_xor(st.l[nt], 16);  // row sum: the 4 lanes of the row
+    l += __shfl_xor(l, 32);
+    const int r = nt * 16 + n;
+    if (r >= R) continue;
+    const int row = out_row(a, b, g, r);
+    const int64_t pi = int64_t(row) * a.parts + part;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      f32x4 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = st.poisoned ? NAN : (l > 0.f ? st.acc[nt][dt][k] / l : 0.f);
+      const int c = 16 * dt + 4 * j;
+      if (final_rows) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) store_f<uint16_t>(out + int64_t(row) * D + c + k, o[k]);
+      } else {
+        *reinterpret_cast<f32x4*>(a.part_o + pi * D + c) = o;
+      }
+    }
+    if (!final_rows && j == 0) {
+      a.part_ml[pi * 2 + 0] = st.poisoned ? NAN : st.m[nt];
+      a.part_ml[pi * 2 + 1] = st.poisoned ? NAN : l;
+    }
+  }
+}
+
 // Balanced schedule. The work of the batch is the list of segments
 // s = b * H_kv + g, each ceil(L_b / 32) steps long, laid end to end; the grid
 // (sized to the resident capacity) splits that list into equal contiguous
@@ -1340,6 +1401,7 @@ struct Plan {
 };
 
 constexpr int kMaxBalancedSeqs = 8192;  // step prefix sums live in LDS
+constexpr int kWavesPerCu = 12;          // resident waves of the one-tile MFMA kernels (3 per SIMD)
 
 int ceil_div(int64_t x, int64_t y) { return int((x + y - 1) / y); }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -1350,6 +1412,7 @@ constexpr int kPerCuMinContext = 6144;  // one workgroup per CU once the longest
 size_t lds_bytes(const Plan& pl, int D, int num_seqs) {
   if (pl.path == PA_PATH_MFMA) {
     const size_t park = size_t(pl.waves) * pl.rows * (D + 2) * sizeof(float);
+    if (pl.sched == PA_SCHED_PARTITIONS_WAVE) return 0;
     if (pl.sched == PA_SCHED_PARTITIONS) return park;
     return size_t((num_seqs + 1 + 3) & ~3) * sizeof(int32_t) + park;  // step prefix sums, then the park area
   }
@@ -1454,7 +1517,12 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   }
   const int parts = ceil_div(d->max_context, pt);
   if (parts > kMaxPartitions) return PA_ERR_UNSUPPORTED;
-  const int64_t grid = pairs * parts;
+  // MFMA path with enough partitions to fill every wave slot of the device
+  // (3 per SIMD) on their own: one wavefront per partition, which streams the
+  // partition without waiting for other waves and writes its partial from
+  // registers; with fewer, the waves of a workgroup share a partition.
+  if (path == PA_PATH_MFMA && pairs * parts >= int64_t(kCUs) * kWavesPerCu) pl->sched = PA_SCHED_PARTITIONS_WAVE;
+  const int64_t grid = pl->sched == PA_SCHED_PARTITIONS_WAVE ? pairs * ceil_div(parts, waves) : pairs * parts;
   if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
   pl->part_tokens = pt;
   pl->parts = parts;
@@ -1462,7 +1530,10 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   pl->merge_grid = parts > 1 ? int(out_rows) : 0;
   pl->segments = 0;
   pl->pieces = 0;
-  pl->ws = parts > 1 ? size_t(out_rows) * parts * (d->head_dim + 2) * sizeof(float) : 0;
+  // partials: (m, l) per row and partition, then o (from a 256-byte boundary, 16-byte stores)
+  pl->ws = parts > 1 ? align256(size_t(out_rows) * parts * 2 * sizeof(float)) +
+                           size_t(out_rows) * parts * d->head_dim * sizeof(float)
+                     : 0;
   return PA_OK;
 }
 
@@ -1481,17 +1552,18 @@ int resident_groups(const void* kernel, int threads, size_t lds) {
 
 // The main kernel a plan launches (one template instance per shape).
 template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE>
-const void* mfma_kernel(bool balanced) {
-  return balanced ? reinterpret_cast<const void*>(mfma_attn_balanced<D, BS, NT, STREAM, KV8, TREE>)
-                  : reinterpret_cast<const void*>(mfma_attn<D, BS, NT, STREAM, KV8, TREE>);
+const void* mfma_kernel(int sched) {
+  if (sched == PA_SCHED_BALANCED) return reinterpret_cast<const void*>(mfma_attn_balanced<D, BS, NT, STREAM, KV8, TREE>);
+  if (sched == PA_SCHED_PARTITIONS_WAVE) return reinterpret_cast<const void*>(mfma_attn_wave<D, BS, NT, STREAM, KV8, TREE>);
+  return reinterpret_cast<const void*>(mfma_attn<D, BS, NT, STREAM, KV8, TREE>);
 }
 
 template <int D, int BS, int NT, bool TREE>
 const void* mfma_kernel(const Plan& pl) {
-  const bool bal = pl.sched == PA_SCHED_BALANCED;
+  const int sc = pl.sched;
   if (pl.kv8)
-    return pl.stream ? mfma_kernel<D, BS, NT, true, true, TREE>(bal) : mfma_kernel<D, BS, NT, false, true, TREE>(bal);
-  return pl.stream ? mfma_kernel<D, BS, NT, true, false, TREE>(bal) : mfma_kernel<D, BS, NT, false, false, TREE>(bal);
+    return pl.stream ? mfma_kernel<D, BS, NT, true, true, TREE>(sc) : mfma_kernel<D, BS, NT, false, true, TREE>(sc);
+  return pl.stream ? mfma_kernel<D, BS, NT, true, false, TREE>(sc) : mfma_kernel<D, BS, NT, false, false, TREE>(sc);
 }
 
 template <int D, int BS, int NT>
@@ -1582,6 +1654,7 @@ pa_status attention_impl(const pa_attn_desc* desc, const void* q, const void* k_
     return PA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (pl.ws > 0 && (!workspace || workspace_bytes < pl.ws)) return PA_ERR_INVALID_ARG;
+  if (pl.ws > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return PA_ERR_INVALID_ARG;  // 16-byte partial stores
   AttnArgs args;
   args.q = q;
   args.k_pool = k_pool;
@@ -1612,7 +1685,8 @@ pa_status attention_impl(const pa_attn_desc* desc, const void* q, const void* k_
   } else if (pl.ws) {
     const int64_t out_rows = int64_t(desc->num_seqs) * q_len * desc->num_q_heads;
     args.part_ml = static_cast<float*>(workspace);
-    args.part_o = static_cast<float*>(workspace) + out_rows * pl.parts * 2;
+    args.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           align256(size_t(out_rows) * pl.parts * 2 * sizeof(float)));
   }
   args.num_seqs = desc->num_seqs;
   args.hq = desc->num_q_heads;

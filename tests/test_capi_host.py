@@ -234,6 +234,18 @@ def test_attention_plan_validation():
     assert pl.schedule == _lib.PA_SCHED_PARTITIONS and pl.num_partitions == 2
     pl = pa.pa_attention_plan(pa.make_desc(**{**ok, "path": pa.PA_PATH_VALU}), 1)
     assert pl.schedule == _lib.PA_SCHED_PARTITIONS
+    # partitions that fill the device's 3072 wave slots on their own: one wavefront each
+    many = {**ok, "num_seqs": 4, "num_kv_heads": 8, "num_q_heads": 64, "block_size": 32,
+            "max_context": 131072, "max_blocks_per_seq": 4096, "num_blocks": 16384, "partition_tokens": 512}
+    pl = pa.pa_attention_plan(pa.make_desc(**many), 1)
+    assert pl.schedule == _lib.PA_SCHED_PARTITIONS_WAVE and pl.num_partitions == 256
+    assert pl.grid == 32 * 256 // 4 and pl.merge_grid == 4 * 64
+    rows_parts = 4 * 64 * 256
+    assert pl.workspace_bytes == -(-rows_parts * 8 // 256) * 256 + rows_parts * 128 * 4
+    assert pa.pa_attention_plan(pa.make_desc(**{**many, "max_context": 3072 * 512 // 32 - 512}),
+                                1).schedule == _lib.PA_SCHED_PARTITIONS
+    assert pa.pa_attention_plan(pa.make_desc(**{**many, "path": pa.PA_PATH_VALU}),
+                                1).schedule == _lib.PA_SCHED_PARTITIONS
     bad = [
         (dict(num_q_heads=7), 1, _lib.PA_ERR_INVALID_ARG),
         (dict(head_dim=96), 1, _lib.PA_ERR_UNSUPPORTED),
