@@ -545,9 +545,10 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     };
     // P.V of one step (the step's only use of the V codes).
     auto accumulate8 = [&](const StepBuf8<D>& buf, int tb, const u32x4 (&pop_hi)[NT],
-                           const u32x4 (&pop_lo)[NT], const float (&alpha)[NT]) {
-      // tokens past the context hold the NaN code: zeroed on every step (a select, no branch)
-      const int valid = min(max(L - (tb + 8 * j), 0), 8);
+                           const u32x4 (&pop_lo)[NT], const float (&alpha)[NT], bool last) {
+      // tokens past the context hold the NaN code: zeroed by a select on the
+      // wave's last step, the only one that can hold the sequence's tail
+      const int valid = last ? min(max(L - (tb + 8 * j), 0), 8) : 8;
       uint32_t keep[4];
 #pragma unroll
       for (int w4 = 0; w4 < 4; ++w4)
@@ -583,7 +584,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
       load_k8(buf, nxt);
       __builtin_amdgcn_sched_barrier(0);
       softmax8(sc, buf, cur.tb, hi, lo, alpha);
-      accumulate8(buf, cur.tb, hi, lo, alpha);
+      accumulate8(buf, cur.tb, hi, lo, alpha, false);
       load_v8(buf, nxt);
       st.poisoned |= !cur.ok;
       cur = nxt;
@@ -593,7 +594,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     float alpha[NT];
     qk8(buf, sc);
     softmax8(sc, buf, cur.tb, hi, lo, alpha);
-    accumulate8(buf, cur.tb, hi, lo, alpha);
+    accumulate8(buf, cur.tb, hi, lo, alpha, true);
     st.poisoned |= !cur.ok;
   } else {
     const int64_t head_stride = int64_t(BS) * D;  // elements of one (block, head) slice
@@ -674,10 +675,13 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     };
 
     // P.V of one step (the step's only use of V).
-    auto accumulate = [&](StepBuf<D>& buf, int tb, const u32x4 (&pop)[NT], const float (&alpha)[NT]) {
+    // last: the wave's last step, the only one that can hold the sequence's
+    // tail (every earlier step of the wave is followed by one inside the
+    // context, so it is full); a compile-time constant at each call.
+    auto accumulate = [&](StepBuf<D>& buf, int tb, const u32x4 (&pop)[NT], const float (&alpha)[NT], bool last) {
       // zero V entries past the context so 0 * NaN never reaches the sum (a
-      // select on every step rather than a branch on the tail step)
-      const int valid = min(max(L - (tb + 8 * j), 0), 8);  // tokens of this lane's 8 still valid
+      // select, not a branch)
+      const int valid = last ? min(max(L - (tb + 8 * j), 0), 8) : 8;  // tokens of this lane's 8 still valid
       uint32_t keep[4];
 #pragma unroll
       for (int w4 = 0; w4 < 4; ++w4)
@@ -718,7 +722,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
       load_k(buf, nxt);
       __builtin_amdgcn_sched_barrier(0);
       softmax(sc, cur.tb, pop, alpha);
-      accumulate(buf, cur.tb, pop, alpha);
+      accumulate(buf, cur.tb, pop, alpha, false);
       load_v(buf, nxt);
       st.poisoned |= !cur.ok;
       cur = nxt;
@@ -728,7 +732,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     float alpha[NT];
     qk(buf, sc);
     softmax(sc, cur.tb, pop, alpha);
-    accumulate(buf, cur.tb, pop, alpha);
+    accumulate(buf, cur.tb, pop, alpha, true);
     st.poisoned |= !cur.ok;
   }
 }
