@@ -66,9 +66,13 @@ class Pool:
     def __init__(self, handle: int):
         self.handle = handle
 
+    # bound at import: a handle that lives until interpreter exit is released
+    # after the module's globals are gone
+    _destroy = staticmethod(lib.pa_pool_destroy)
+
     def __del__(self):
         if getattr(self, "handle", None):
-            lib.pa_pool_destroy(self.handle)
+            self._destroy(self.handle)
             self.handle = None
 
 
@@ -79,9 +83,11 @@ class PrefixCache:
         self.handle = handle
         self.pool = pool
 
+    _destroy = staticmethod(lib.pa_prefix_cache_destroy)  # bound at import, as for Pool
+
     def __del__(self):
-        if getattr(self, "handle", None) and getattr(self.pool, "handle", None):
-            lib.pa_prefix_cache_destroy(self.handle)
+        if getattr(self, "handle", None) and getattr(getattr(self, "pool", None), "handle", None):
+            self._destroy(self.handle)
             self.handle = None
 
 

@@ -26,17 +26,22 @@
 //               partition_tokens tokens); partitions write partials and
 //               lse_merge combines them (sequence-parallel attention: local
 //               attention per KV segment, then a reduction; "Mở rộng Quy mô
-//               và Triển khai", "Song song hóa Chuỗi").
+//               và Triển khai", "Song song hóa Chuỗi"). When the partitions
+//               alone fill the device's wave slots, a wavefront per partition
+//               instead, its partial written from registers.
 //
 // Kernels:
-//   mfma_attn_balanced, mfma_attn  bf16 queries. Per 32-token step, scores
+//   mfma_attn_balanced, mfma_attn, mfma_attn_wave  bf16 queries. Per 32-token step, scores
 //              S^T[token][row] come from v_mfma_f32_16x16x32_bf16 with the K
 //              rows as the A operand and the query rows as B; the output
 //              accumulator O^T[d][row] from the same instruction with the
 //              V^T slice as A and the bf16 probabilities as B. Each lane owns
 //              one query row (lane % 16), so the softmax rescale is
 //              lane-local; only the per-step row maximum crosses lanes. One
-//              or two 16-row tiles (NT). Template variants: FP8 E4M3 pools
+//              or two 16-row tiles (NT). A wave keeps one K and one V
+//              register buffer and refills each with the next step's loads
+//              as soon as the step has consumed it (next K after the score
+//              MFMAs, next V during P.V). Template variants: FP8 E4M3 pools
 //              (KV8: codes converted to bf16 in registers, per-token scales on
 //              the scores and the P.V weights), tree masks over the drafted
 //              positions (TREE), non-temporal K/V loads (STREAM).
