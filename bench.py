@@ -203,7 +203,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published (no sparsit
 SIMD_CLOCK_GHZ = 2.4             # MI355X peak engine clock
 
 
-def counter_summary(workload: str, run_dirs, bench_json: str):
+def counter_summary(workload: str, run_dirs, bench_json: str, out_dir: str = None):
     """Per-launch means of the main kernel's rocprofv3 --pmc counters (one or
     more runs of bench.py, derived metrics such as MfmaUtil, MfmaFlopsBF16,
     VALUBusy, OccupancyPercent allowed) written to
@@ -234,17 +234,18 @@ def counter_summary(workload: str, run_dirs, bench_json: str):
         if "flops" in rec:
             out["algorithmic_flops"] = rec["flops"]
             out["mfma_flops_over_algorithmic"] = flops / rec["flops"]
-    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"counters_{workload}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out, indent=1))
+    return out
 
 
-def committed_counters(workload: str, kernel: str):
+def committed_counters(workload: str, kernel: str, profiles_dir: str = None):
     """MFMA and VALU utilisation of the main kernel from committed rocprofv3
     counter runs, if they were taken on the current sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    path = os.path.join(profiles_dir or os.path.join(ROOT, "profiles"), f"counters_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
