@@ -88,6 +88,7 @@ def cpu_baseline(w, budget_s: float = 15.0):
                   f"{t_used:.1f} s; numpy fp64 with {blas_threads} BLAS threads on {affinity} visible cores",
         "seconds": round(t_used, 3),
         "tokens_per_s": round(done * cfg.q_len / t_used, 3),
+        "affinity_cores": affinity, "cpu_count": os.cpu_count(), "blas_threads": blas_threads,
     }
 
 
