@@ -264,6 +264,11 @@ def test_attention_plan_validation():
         (dict(kv_format=2), 1, _lib.PA_ERR_INVALID_ARG),
         (dict(kv_format=pa.PA_KV_FP8_E4M3, path=pa.PA_PATH_VALU), 1, _lib.PA_ERR_UNSUPPORTED),
         (dict(kv_format=pa.PA_KV_FP8_E4M3, dtype=pa.PA_DTYPE_F32), 1, _lib.PA_ERR_UNSUPPORTED),
+        (dict(num_seqs=0), 1, _lib.PA_ERR_INVALID_ARG),            # empty batch
+        (dict(num_kv_heads=0), 1, _lib.PA_ERR_INVALID_ARG),
+        (dict(num_blocks=0), 1, _lib.PA_ERR_INVALID_ARG),          # empty pool
+        (dict(max_blocks_per_seq=0), 1, _lib.PA_ERR_INVALID_ARG),
+        (dict(max_context=0), 1, _lib.PA_ERR_INVALID_ARG),
     ]
     for over, q_len, status in bad:
         with pytest.raises(pa.PAError) as e:
@@ -310,6 +315,27 @@ def test_attention_tree_rejects_bad_masks_before_launch():
     assert call(4, fake, 3) == _lib.PA_ERR_INVALID_ARG          # rows of one sequence overlap the next
     assert call(4, fake, -1) == _lib.PA_ERR_INVALID_ARG
     assert call(0, fake, 0) == _lib.PA_ERR_INVALID_ARG
+
+
+def test_attention_rejects_small_or_misaligned_workspace_before_launch():
+    """The split-KV partials need a workspace of the reported size, 16-byte
+    aligned; anything else is refused before any device work (the pointers
+    below are never dereferenced)."""
+    import ctypes as C
+    desc = pa.make_desc(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                        max_blocks_per_seq=8, num_blocks=32, dtype=pa.PA_DTYPE_BF16, max_context=128,
+                        partition_tokens=64)
+    size = pa.pa_attention_workspace_size(desc, 1)
+    assert size > 0
+    fake = 256
+
+    def call(ws, nbytes):
+        return _lib.lib.pa_attention(C.byref(desc), fake, fake, fake, fake, fake, 1, 1.0, fake, ws, nbytes, None)
+    assert call(None, size) == _lib.PA_ERR_INVALID_ARG          # no workspace
+    assert call(4096, size - 1) == _lib.PA_ERR_INVALID_ARG      # too small
+    assert call(4096 + 8, size) == _lib.PA_ERR_INVALID_ARG      # 8-byte aligned only
+    assert _lib.lib.pa_attention(C.byref(desc), fake, fake, fake, fake, fake, 1, float("nan"), fake, 4096,
+                                 size, None) == _lib.PA_ERR_INVALID_ARG
 
 
 def test_one_hip_runtime_per_process():
