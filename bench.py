@@ -200,6 +200,29 @@ def _pmc_finish(out, fetch_dir, write_dir, copy_bytes, kernel, workload):
     print(json.dumps(out, indent=1))
 
 
+def trace_summary(run_dir: str, kernel: str, skip: int, take: int = 0):
+    """Per-dispatch durations of `kernel` from a rocprofv3 --kernel-trace run
+    (run_kernel_trace.csv in run_dir), in dispatch order, with the first
+    `skip` dispatches (the warm-up calls) dropped and at most `take` kept
+    (0: all the rest): the steady-state figures of the timed region."""
+    import csv
+    import statistics
+    rows = [r for r in csv.DictReader(open(os.path.join(run_dir, "run_kernel_trace.csv")))
+            if kernel in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    keep = rows[skip:skip + take] if take else rows[skip:]
+    if not keep:
+        raise SystemExit(f"{run_dir}: no {kernel} dispatches after the first {skip}")
+    us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in keep]
+    span = (int(keep[-1]["End_Timestamp"]) - int(keep[0]["Start_Timestamp"])) / 1e3
+    out = {"kernel": kernel, "dispatches_total": len(rows), "skipped": skip, "kept": len(us),
+           "mean_us": round(statistics.mean(us), 2), "median_us": round(statistics.median(us), 2),
+           "min_us": round(min(us), 2), "max_us": round(max(us), 2),
+           "span_per_dispatch_us": round(span / len(us), 2)}
+    print(json.dumps(out))
+    return out
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published (no sparsity)
 SIMD_CLOCK_GHZ = 2.4             # MI355X peak engine clock
 
@@ -278,37 +301,81 @@ def attention_flops(cfg, lens, tree_parents=None) -> int:
 
 
 def read_probe(gib: int = 4, reps: int = 10):
-    """Practical HBM read ceiling: the library's read probe over a `gib` GiB
-    buffer read once per call as 8 KiB blocks in a seeded random order (the
-    attention kernels' access pattern), over a few launch shapes; the best
-    rate is the ceiling the attention kernels are compared with."""
+    """Practical HBM read ceilings: the library's read probe over a `gib` GiB
+    buffer read once per call as 8 KiB blocks, over a few launch shapes, in
+    two orders: a seeded random permutation (the attention kernels' access
+    pattern: each (block, KV head) slice is one 8 KiB block somewhere in the
+    pool) and ascending (a contiguous streaming read). The best random-order
+    rate is the ceiling the attention kernels are compared with; the
+    streaming rate says what the random order costs."""
     import torch
     import paged_kv_cache_218_amd as pa
     n_blocks = gib * 2**30 // 8192
     buf = torch.ones(n_blocks * 8192, dtype=torch.uint8, device="cuda")
     gen = torch.Generator().manual_seed(218)
-    order = torch.randperm(n_blocks, generator=gen).to(torch.int32).cuda()
+    orders = {"random": torch.randperm(n_blocks, generator=gen).to(torch.int32).cuda(),
+              "sequential": torch.arange(n_blocks, dtype=torch.int32, device="cuda")}
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     rows = []
-    for depth in (1, 2, 4):
-        for waves_per_cu in (8, 16, 32):
-            wgs = 256 * waves_per_cu // 4
-            for _ in range(2):
-                pa.pa_read_probe(buf, order, depth, wgs, sink)
-            torch.cuda.synchronize()
-            e0.record()
-            for _ in range(reps):
-                pa.pa_read_probe(buf, order, depth, wgs, sink)
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) / reps * 1e3
-            rows.append({"blocks_in_flight": depth, "workgroups": wgs, "us": round(us, 1),
-                         "gbs": round(n_blocks * 8192 / us / 1e3, 1)})
-            log(f"read probe: {depth} blocks in flight per wave, {wgs} workgroups: {us:.1f} us, {rows[-1]['gbs']} GB/s")
-    best = max(rows, key=lambda r: r["gbs"])
+    for name, order in orders.items():
+        for depth in (1, 2, 4):
+            for waves_per_cu in (8, 16, 32):
+                wgs = 256 * waves_per_cu // 4
+                for _ in range(2):
+                    pa.pa_read_probe(buf, order, depth, wgs, sink)
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(reps):
+                    pa.pa_read_probe(buf, order, depth, wgs, sink)
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / reps * 1e3
+                rows.append({"order": name, "blocks_in_flight": depth, "workgroups": wgs, "us": round(us, 1),
+                             "gbs": round(n_blocks * 8192 / us / 1e3, 1)})
+                log(f"read probe ({name}): {depth} blocks in flight per wave, {wgs} workgroups: {us:.1f} us, "
+                    f"{rows[-1]['gbs']} GB/s")
+    best = max((r for r in rows if r["order"] == "random"), key=lambda r: r["gbs"])
+    best_seq = max((r for r in rows if r["order"] == "sequential"), key=lambda r: r["gbs"])
     return {"bytes": n_blocks * 8192, "order": "seeded random permutation of 8 KiB blocks",
-            "best_gbs": best["gbs"], "best_frac_of_8tbs": round(best["gbs"] / 8000, 4), "runs": rows}
+            "best_gbs": best["gbs"], "best_frac_of_8tbs": round(best["gbs"] / 8000, 4),
+            "sequential_best_gbs": best_seq["gbs"], "sequential_best_frac_of_8tbs": round(best_seq["gbs"] / 8000, 4),
+            "runs": rows}
+
+
+def host_timing(call, plan_call, calls: int = 1000):
+    """CPU time per call of the library, measured with perf_counter_ns around
+    each of `calls` back-to-back asynchronous calls (no synchronisation inside
+    the loop; the kernels queue up behind each other on the stream), through
+    ctypes with the arguments converted once beforehand. plan_call is a
+    host-only entry point taking the same descriptor (it plans, launches
+    nothing), timed the same way: the difference is what a launch adds."""
+    import statistics
+    import torch
+
+    def run(fn):
+        ts = []
+        for _ in range(calls):
+            t0 = time.perf_counter_ns()
+            st = fn()
+            ts.append(time.perf_counter_ns() - t0)
+            if st:
+                raise SystemExit(f"host timing: status {st}")
+        return ts
+
+    torch.cuda.synchronize()
+    launch = run(call)
+    torch.cuda.synchronize()
+    plan = run(plan_call)
+    q = lambda ts, f: sorted(ts)[int(f * (len(ts) - 1))] / 1e3
+    return {"calls": calls,
+            "us_per_call_median": round(statistics.median(launch) / 1e3, 2),
+            "us_per_call_mean": round(statistics.mean(launch) / 1e3, 2),
+            "us_per_call_p99": round(q(launch, 0.99), 2),
+            "plan_only_us_median": round(statistics.median(plan) / 1e3, 2),
+            "how": "perf_counter_ns around each raw ctypes call of the entry point, arguments pre-converted; "
+                   "asynchronous calls back to back; plan_only = pa_attention_workspace_size on the same "
+                   "descriptor (host planning, no launch)"}
 
 
 def _sub_cfg(cfg, batch):
@@ -425,6 +492,8 @@ def main():
                     help="-1: the workload's own setting; 0: library's choice")
     ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup (0: library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--host-calls", type=int, default=1000,
+                    help="after the timed region, time this many calls on the CPU side (0: skip)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--read-probe", action="store_true",
                     help="measure the device's read ceiling (8 KiB blocks in random order) and exit")
@@ -435,7 +504,15 @@ def main():
     ap.add_argument("--counter-summary", nargs="+", metavar="RUN_DIR",
                     help="write profiles/counters_<workload>.json from rocprofv3 --pmc runs (utilisation "
                          "counters) and a --bench-json line, and exit")
+    ap.add_argument("--trace-summary", metavar="RUN_DIR",
+                    help="steady-state durations of --kernel from a rocprofv3 --kernel-trace run and exit")
+    ap.add_argument("--kernel", help="with --trace-summary: kernel name (substring)")
+    ap.add_argument("--skip", type=int, default=0, help="with --trace-summary: leading dispatches to drop")
+    ap.add_argument("--take", type=int, default=0, help="with --trace-summary: dispatches to keep (0: all)")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.kernel, args.skip, args.take)
+        return
     if args.pmc_summary:
         pmc_summary(args.workload, *args.pmc_summary, bench_json=args.bench_json)
         return
@@ -562,6 +639,23 @@ def main():
     counters = committed_counters(cfg.name, kernel)
     if counters is not None:
         result["roofline"]["counters"] = counters
+    if args.host_calls > 0:
+        import ctypes as C
+        lib = pa._lib.lib
+        ws_arg = ws.data_ptr() if plan.workspace_bytes else None
+        ws_n = plan.workspace_bytes
+        ptrs = [t.data_ptr() for t in (q, cache.k_pool, cache.v_pool, tables_d, lens_d)]
+        desc_ref, sid, out_p = C.byref(desc), stream.cuda_stream, out.data_ptr()
+        if masks is None:
+            call = lambda: lib.pa_attention(desc_ref, *ptrs, cfg.q_len, cfg.scale, out_p, ws_arg, ws_n, sid)
+        else:
+            mp = masks.data_ptr()
+            call = lambda: lib.pa_attention_tree(desc_ref, *ptrs, cfg.q_len, mp, cfg.q_len, cfg.scale, out_p,
+                                                 ws_arg, ws_n, sid)
+        ql = cfg.q_len
+        plan_call = lambda: 0 if lib.pa_attention_workspace_size(desc_ref, ql) == plan.workspace_bytes else 1
+        log(f"host timing: {args.host_calls} calls")
+        result["host_timing"] = host_timing(call, plan_call, args.host_calls)
     if args.copy_probe:
         result["copy_probe"] = copy_probe()
     if not args.no_cpu_baseline:

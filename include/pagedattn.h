@@ -154,8 +154,15 @@ int64_t pa_pool_buffer_bytes(int32_t num_blocks, int32_t block_size, int32_t num
 int64_t pa_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
                               int32_t elem_bytes);
 
-/* Pop the head of the free list into *block_id and set its count to 1.
- * PA_ERR_NO_FREE_BLOCK when the list is empty (state unchanged). */
+/* Pop the head of the free list into *block_id and set its count to 1: a
+ * sequence that grows past a multiple of the block size asks the free pool
+ * for one more physical block [Blog #54 question 2: a new block is requested
+ * from the free block pool each time the current one fills; Part 8,
+ * "PagedAttention: Ảo Hóa Phân Trang Bộ Nhớ Cho Key và Value": blocks are
+ * handed out on demand]. With a prefix cache attached, an empty free list
+ * evicts the least recently used unreferenced cached block instead.
+ * PA_ERR_NO_FREE_BLOCK when no block can be supplied (state unchanged);
+ * PA_ERR_INVALID_ARG for a NULL pool or block_id. */
 pa_status pa_block_alloc(pa_pool* pool, int32_t* block_id);
 
 /* Share a live block: count += 1 [Blog #54 question 2: sharers point at the
@@ -243,7 +250,12 @@ typedef struct pa_attn_desc {
                                  for up to 8192 sequences, else PARTITIONS); otherwise
                                  PARTITIONS of this many tokens, a multiple of 64 */
   int32_t waves_per_group;    /* wavefronts per workgroup of the main kernel: 0 = chosen
-                                 by the library, else 1, 2 or 4 */
+                                 by the library; else 1, 2 or 4 for the PARTITIONS
+                                 schedules, and 1, 2, 4, 8 or 12 for BALANCED (12 with
+                                 one 16-row query tile, G*q_len <= 16; at most 8 with
+                                 two). Larger values than the schedule allows give
+                                 PA_ERR_UNSUPPORTED, values outside the list
+                                 PA_ERR_INVALID_ARG */
   int32_t kv_shared;          /* cache hint, results do not depend on it: 0 = every
                                  physical block is read by one sequence only, so K/V
                                  loads stream past the caches; 1 = some blocks are
@@ -274,11 +286,28 @@ typedef struct pa_attn_plan {
  * PA_ERR_UNSUPPORTED exactly where pa_attention would fail validation. */
 pa_status pa_attention_plan(const pa_attn_desc* desc, int32_t q_len, pa_attn_plan* plan);
 
-/* Workspace bytes pa_attention needs (0 when no partition merge is needed),
- * or 0 for an invalid descriptor. */
+/* Workspace bytes pa_attention needs for this descriptor and q_len: the
+ * split-KV partials of sequence-parallel attention, each partition's (m, l, o)
+ * kept until the log-sum-exp reduction combines them ["Mở rộng Quy mô và
+ * Triển khai", "Song song hóa Chuỗi": attention local to each KV segment,
+ * then a reduction; Part 8, "Thực Thi Kernel Toán Học Trong CUDA": the
+ * running maximum and sum of the online softmax are what a partial carries].
+ * 0 when nothing is split, or for an invalid descriptor. The size does not
+ * depend on the device: the balanced schedule's share is bounded for at most
+ * 256 compute units (a larger device runs that many resident workgroups at
+ * most). Layout, the same for every schedule: align256(4*num_seqs*
+ * num_kv_heads) bytes of arrival counters, written by the BALANCED schedule
+ * only; then the (m, l) partials; then, from a 256-byte boundary, the o
+ * partials. */
 size_t pa_attention_workspace_size(const pa_attn_desc* desc, int32_t q_len);
 
-/* Paged attention for q_len query rows per sequence.
+/* Paged attention for q_len query rows per sequence [Part 8, "Thực Thi
+ * Kernel Toán Học Trong CUDA": A_i = softmax(q_i K^T / sqrt(d_k)), computed
+ * block by block over the blocks B_1..B_m the block table names, with the
+ * running maximum, running sum and rescaled output of an online softmax;
+ * Blog #54 section 2.2: the kernel reads the block table itself; Blog #54
+ * section 2.4 and Part 8's speculative-decoding diagram: q_len > 1 scores all
+ * drafted tokens in one pass].
  *   q            device [B][q_len][H_q][d]
  *   k_pool       device pool layout above; v_pool likewise
  *   block_tables device int32 [B][max_blocks_per_seq]; entries past a
@@ -292,10 +321,16 @@ size_t pa_attention_workspace_size(const pa_attn_desc* desc, int32_t q_len);
  *   workspace    device, >= pa_attention_workspace_size bytes, 16-byte aligned
  *                (may be NULL when that size is 0); holds split-KV partials, no
  *                hidden allocation.
- *                With the BALANCED schedule its first bytes are arrival
- *                counters: the workspace must be zero-filled before its first
- *                use, and every completed call leaves them zero again. Calls
- *                that share one workspace must not run concurrently.
+ *                Its first align256(4*B*H_kv) bytes are the BALANCED
+ *                schedule's arrival counters, which must be zero when such a
+ *                call starts. Only that schedule writes them, and every
+ *                completed call leaves them zero; every other layout starts
+ *                its partials after them. So a workspace zero-filled once
+ *                serves any sequence of calls (any schedule, path or q_len)
+ *                whose B*H_kv never grows; after a call with a smaller B*H_kv
+ *                wrote partials there, zero-fill it again before a BALANCED
+ *                call with a larger one. Calls that share one workspace must
+ *                not run concurrently.
  * Output row (b, i, h) = softmax(scale * q[b,i,h] . K_b[t], t visible) . V_b.
  * Requirements (else PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED, nothing
  * launched): H_q % H_kv == 0, d in {64,128}, bs in {16,32}, 1 <= q_len,

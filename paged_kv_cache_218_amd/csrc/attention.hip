@@ -55,6 +55,8 @@
 
 #include <algorithm>
 #include <cmath>
+#include <atomic>
+#include <mutex>
 
 #include "pa_internal.h"
 
@@ -76,7 +78,7 @@ extern "C" const char* pa_hip_error_name(int32_t hip_error) {
 
 namespace {
 
-constexpr int kCUs = 256;              // MI355X compute units
+constexpr int kMaxCUs = 256;           // compute units the workspace bound allows for (MI355X: 256)
 constexpr int kMaxPartitions = 1 << 16;  // partitions per sequence
 constexpr int kMfmaMaxRows = 32;       // two 16-row tiles
 constexpr int kValuMaxRows = 16;
@@ -1406,7 +1408,12 @@ struct Plan {
   bool kv8;     // FP8 pools
   bool tree;    // per-row visibility masks over the drafted positions
   int64_t segments, pieces;  // balanced schedule: segments, partial slots
-  size_t ws;
+  // Workspace layout, the same for every schedule: the balanced schedule's
+  // arrival counters (ws_counters bytes, reserved by every layout so that no
+  // other schedule ever writes them), then the partials: (m, l) pairs at
+  // offset 0 of the partial area, o from offset ws_o_off.
+  size_t ws_counters, ws_o_off, ws_partials;
+  size_t ws;  // total: ws_counters + ws_partials, or 0 when nothing is split
 };
 
 constexpr int kMaxBalancedSeqs = 8192;  // step prefix sums live in LDS
@@ -1441,6 +1448,27 @@ int default_waves(const Plan& pl, int max_context) {
   if (pl.sched == PA_SCHED_BALANCED && pl.nt == 1 && max_context >= kPerCuMinContext)
     return balanced_waves(pl.nt);
   return 4;
+}
+
+// Compute units of the current device, queried once per device and kept
+// (kMaxCUs when no device can be queried). Used to size partitions; the
+// workspace bound does not depend on it.
+constexpr int kMaxDevices = 64;
+int device_cus() {
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kMaxCUs;
+  }
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return kMaxCUs;
+  }
+  cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
@@ -1501,24 +1529,26 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   if (balanced) {
     // grid = resident capacity; the workspace is sized for the largest one
     // (every compute unit full of single-workgroup waves)
-    const int64_t grid_max = int64_t(kCUs) * std::max(1, 32 / waves);
+    const int64_t grid_max = int64_t(kMaxCUs) * std::max(1, 32 / waves);
     pl->part_tokens = 0;
     pl->parts = 0;
     pl->grid = int(grid_max);
     pl->merge_grid = 0;
     pl->segments = pairs;
     pl->pieces = grid_max + pairs;
-    pl->ws = align256(size_t(pairs) * sizeof(int32_t)) +
-             align256(size_t(pl->pieces) * rows * 2 * sizeof(float)) +
-             size_t(pl->pieces) * rows * d->head_dim * sizeof(float);
+    pl->ws_counters = align256(size_t(pairs) * sizeof(int32_t));
+    pl->ws_o_off = align256(size_t(pl->pieces) * rows * 2 * sizeof(float));
+    pl->ws_partials = pl->ws_o_off + size_t(pl->pieces) * rows * d->head_dim * sizeof(float);
+    pl->ws = pl->ws_counters + pl->ws_partials;
     return PA_OK;
   }
+  const int cus = device_cus();
   int pt = d->partition_tokens;
   if (pt == 0) {
     // enough waves for two full rounds of the kernel's occupancy (the VALU
     // kernel runs 16 waves per compute unit; the MFMA one 12), partitions of
     // at least 256 tokens
-    const int64_t target = int64_t(kCUs) * (path == PA_PATH_VALU ? 32 : 24);
+    const int64_t target = int64_t(cus) * (path == PA_PATH_VALU ? 32 : 24);
     const int64_t want = (target + pairs * waves - 1) / (pairs * waves);
     const int max_parts = std::max(1, ceil_div(d->max_context, 256));
     const int parts = int(std::min<int64_t>(std::max<int64_t>(want, 1), max_parts));
@@ -1530,7 +1560,7 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   // (3 per SIMD) on their own: one wavefront per partition, which streams the
   // partition without waiting for other waves and writes its partial from
   // registers; with fewer, the waves of a workgroup share a partition.
-  if (path == PA_PATH_MFMA && pairs * parts >= int64_t(kCUs) * kWavesPerCu) pl->sched = PA_SCHED_PARTITIONS_WAVE;
+  if (path == PA_PATH_MFMA && pairs * parts >= int64_t(cus) * kWavesPerCu) pl->sched = PA_SCHED_PARTITIONS_WAVE;
   const int64_t grid = pl->sched == PA_SCHED_PARTITIONS_WAVE ? pairs * ceil_div(parts, waves) : pairs * parts;
   if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
   pl->part_tokens = pt;
@@ -1539,23 +1569,50 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   pl->merge_grid = parts > 1 ? int(out_rows) : 0;
   pl->segments = 0;
   pl->pieces = 0;
-  // partials: (m, l) per row and partition, then o (from a 256-byte boundary, 16-byte stores)
-  pl->ws = parts > 1 ? align256(size_t(out_rows) * parts * 2 * sizeof(float)) +
-                           size_t(out_rows) * parts * d->head_dim * sizeof(float)
-                     : 0;
+  // partials: (m, l) per row and partition, then o (from a 256-byte boundary,
+  // 16-byte stores), after the counter area of the balanced schedule, which
+  // this schedule leaves untouched
+  if (parts > 1) {
+    pl->ws_counters = align256(size_t(pairs) * sizeof(int32_t));
+    pl->ws_o_off = align256(size_t(out_rows) * parts * 2 * sizeof(float));
+    pl->ws_partials = pl->ws_o_off + size_t(out_rows) * parts * d->head_dim * sizeof(float);
+  } else {
+    pl->ws_counters = pl->ws_o_off = pl->ws_partials = 0;
+  }
+  pl->ws = pl->ws_counters + pl->ws_partials;
   return PA_OK;
 }
 
 
-// Workgroups of `kernel` that fit on the device at once (0 if unknown).
+// Workgroups of `kernel` that fit on the device at once (0 if unknown). The
+// occupancy query runs once per (kernel, threads, LDS bytes, device); later
+// calls read the kept answer.
 int resident_groups(const void* kernel, int threads, size_t lds) {
-  int per_cu = 0, dev = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess ||
-      hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+  struct Entry { const void* kernel; int threads; size_t lds; int dev, per_cu; };
+  static std::mutex mu;
+  static Entry seen[256];
+  static int n_seen = 0, next_slot = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
+  const int cus = device_cus();
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n_seen; ++i)
+      if (seen[i].kernel == kernel && seen[i].threads == threads && seen[i].lds == lds && seen[i].dev == dev)
+        return seen[i].per_cu * cus;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  seen[next_slot] = Entry{kernel, threads, lds, dev, per_cu};  // a full table recycles its oldest entry
+  next_slot = (next_slot + 1) % 256;
+  n_seen = std::min(n_seen + 1, 256);
   return per_cu * cus;
 }
 
@@ -1684,18 +1741,11 @@ pa_status attention_impl(const pa_attn_desc* desc, const void* q, const void* k_
     args.k_scales = reinterpret_cast<const float*>(static_cast<const char*>(k_pool) + codes);
     args.v_scales = reinterpret_cast<const float*>(static_cast<const char*>(v_pool) + codes);
   }
-  if (pl.sched == PA_SCHED_BALANCED) {
+  if (pl.ws) {
     char* w = static_cast<char*>(workspace);
-    args.counters = reinterpret_cast<int32_t*>(w);
-    w += align256(size_t(pl.segments) * sizeof(int32_t));
-    args.part_ml = reinterpret_cast<float*>(w);
-    w += align256(size_t(pl.pieces) * pl.rows * 2 * sizeof(float));
-    args.part_o = reinterpret_cast<float*>(w);
-  } else if (pl.ws) {
-    const int64_t out_rows = int64_t(desc->num_seqs) * q_len * desc->num_q_heads;
-    args.part_ml = static_cast<float*>(workspace);
-    args.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                           align256(size_t(out_rows) * pl.parts * 2 * sizeof(float)));
+    if (pl.sched == PA_SCHED_BALANCED) args.counters = reinterpret_cast<int32_t*>(w);
+    args.part_ml = reinterpret_cast<float*>(w + pl.ws_counters);
+    args.part_o = reinterpret_cast<float*>(w + pl.ws_counters + pl.ws_o_off);
   }
   args.num_seqs = desc->num_seqs;
   args.hq = desc->num_q_heads;

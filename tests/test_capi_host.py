@@ -241,7 +241,8 @@ def test_attention_plan_validation():
     assert pl.schedule == _lib.PA_SCHED_PARTITIONS_WAVE and pl.num_partitions == 256
     assert pl.grid == 32 * 256 // 4 and pl.merge_grid == 4 * 64
     rows_parts = 4 * 64 * 256
-    assert pl.workspace_bytes == -(-rows_parts * 8 // 256) * 256 + rows_parts * 128 * 4
+    # the balanced schedule's counter area (4 x 8 pairs, one 256-byte unit) comes first in every layout
+    assert pl.workspace_bytes == 256 + -(-rows_parts * 8 // 256) * 256 + rows_parts * 128 * 4
     assert pa.pa_attention_plan(pa.make_desc(**{**many, "max_context": 3072 * 512 // 32 - 512}),
                                 1).schedule == _lib.PA_SCHED_PARTITIONS
     assert pa.pa_attention_plan(pa.make_desc(**{**many, "path": pa.PA_PATH_VALU}),
@@ -278,7 +279,7 @@ def test_attention_plan_validation():
     d = pa.make_desc(4, 64, 8, 128, 32, 4096, 16384, pa.PA_DTYPE_BF16, 131072, partition_tokens=512)
     pl = pa.pa_attention_plan(d, 1)
     assert (pl.num_partitions, pl.merge_grid) == (256, 4 * 64)
-    assert pl.workspace_bytes == 4 * 64 * 256 * (128 + 2) * 4
+    assert pl.workspace_bytes == 256 + 4 * 64 * 256 * (128 + 2) * 4
     assert pa.pa_attention_workspace_size(d, 1) == pl.workspace_bytes
 
 

@@ -141,6 +141,32 @@ def test_balanced_repeat_calls_reuse_workspace(key):
             assert np.array_equal(out_bits(o), first)
 
 
+@pytest.mark.parametrize("key", ["long", "8b"])
+def test_schedules_share_one_workspace(key):
+    """One cache, one workspace, calls alternating between schedules: the
+    balanced schedule's arrival counters sit in an area no other schedule
+    writes, so a balanced call after partition calls (whose partials fill the
+    rest of the workspace) still merges its split sequences. Every call
+    matches the oracle and leaves the counters zero."""
+    import paged_kv_cache_218_amd as pa
+    w, ref = small(key)
+    cfg = w.cfg
+    from paged_kv_cache_218_amd.cache import PagedKVCache
+    cache = PagedKVCache.from_workload(w)
+    seq = [(MFMA, 0), (MFMA, 128), (VALU, 64), (MFMA, 0), (MFMA, 64), (MFMA, 0)]
+    scheds = []
+    for path, pt in seq:
+        print(f"{key}: path {path} partition_tokens {pt}", flush=True)
+        out, _ = run_gpu(w, path=path, partition_tokens=pt, cache=cache)
+        desc = cache.desc(cfg.num_q_heads, int(w.lens.max()), path, pt, 0)
+        plan = pa.pa_attention_plan(desc, cfg.q_len)
+        scheds.append(plan.schedule)
+        assert_close(out_to_f64(out, cfg.dtype), ref, cfg.dtype, f"{key} path {path} pt {pt}")
+        counters = cache._ws[:cfg.batch * cfg.num_kv_heads * 4]
+        assert int(counters.count_nonzero()) == 0
+    assert scheds.count(pa.PA_SCHED_BALANCED) == 3 and pa.PA_SCHED_PARTITIONS in scheds
+
+
 @pytest.mark.parametrize("key", ["8b", "verify", "tiny_f32", "verify_fp8", "d64_fp8"])
 def test_pool_bytes_and_tables_match_model(key):
     """pa_write_kv (allocation, copy-on-write, scatter, FP8 quantisation) gives
