@@ -80,8 +80,10 @@ enum {
   PA_ERR_NO_FREE_BLOCK = 3, /* the pool cannot supply the blocks asked for */
   PA_ERR_BAD_BLOCK = 4,     /* refcount underflow, fork/free of a free block */
   PA_ERR_HIP = 5,           /* a HIP runtime call or kernel launch failed */
-  PA_ERR_NO_MEMORY = 6      /* host memory for the bookkeeping could not be allocated;
+  PA_ERR_NO_MEMORY = 6,     /* host memory for the bookkeeping could not be allocated;
                                the call changed nothing */
+  PA_ERR_TOO_LARGE = 7      /* the call needs more scratch than pa_attention_noalloc
+                               holds; nothing launched */
 };
 
 enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1, PA_DTYPE_FP8_E4M3 = 2 };
@@ -342,6 +344,26 @@ pa_status pa_attention(const pa_attn_desc* desc, const void* q, const void* k_po
                        const void* v_pool, const int32_t* block_tables,
                        const int32_t* context_lens, int32_t q_len, float scale, void* out,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* pa_attention for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as pa_attention, without the workspace:
+ * split-KV state lives in a scratch array inside this library, one per GPU,
+ * PA_NOALLOC_SCRATCH_BYTES long, held from the first call on that GPU until
+ * the process ends. Its first 256 KiB are the balanced schedule's arrival
+ * counters (up to 65,536 (sequence, KV head) pairs), zeroed on the stream by
+ * a small kernel at the start of every call that uses them; the rest holds
+ * the partials (at most pa_attention_workspace_size minus its counter area).
+ * A call needing more returns PA_ERR_TOO_LARGE before any device work. The
+ * call allocates nothing, host or device. Every call on one GPU shares that
+ * GPU's scratch and leaves its contents there: calls that may overlap on one
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller. */
+enum { PA_NOALLOC_SCRATCH_BYTES = 64 << 20 };
+pa_status pa_attention_noalloc(const pa_attn_desc* desc, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t q_len, float scale,
+                               void* out, void* stream);
 
 /* Tree-structured verification ("Mở rộng Quy mô và Triển khai", section
  * "Giải mã Suy đoán", its variants: parallel decoding drafts a tree of

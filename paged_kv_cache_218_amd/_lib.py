@@ -10,7 +10,9 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_NO_FREE_BLOCK, PA_ERR_BAD_BLOCK, PA_ERR_HIP, PA_ERR_NO_MEMORY = range(7)
+(PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_NO_FREE_BLOCK, PA_ERR_BAD_BLOCK, PA_ERR_HIP, PA_ERR_NO_MEMORY,
+ PA_ERR_TOO_LARGE) = range(8)
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20
 PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3 = 0, 1, 2
 PA_KV_SAME, PA_KV_FP8_E4M3 = 0, 1
 PA_PATH_AUTO, PA_PATH_VALU, PA_PATH_MFMA = 0, 1, 2
@@ -54,6 +56,7 @@ SIGNATURES = [
     ("pa_attention_plan", i32, [C.POINTER(AttnDesc), i32, C.POINTER(AttnPlan)]),
     ("pa_attention_workspace_size", sz, [C.POINTER(AttnDesc), i32]),
     ("pa_attention", i32, [C.POINTER(AttnDesc), vp, vp, vp, vp, vp, i32, f32, vp, vp, sz, vp]),
+    ("pa_attention_noalloc", i32, [C.POINTER(AttnDesc), vp, vp, vp, vp, vp, i32, f32, vp, vp]),
     ("pa_attention_tree", i32, [C.POINTER(AttnDesc), vp, vp, vp, vp, vp, i32, vp, i32, f32, vp, vp, sz, vp]),
     ("pa_tree_masks", i32, [pi32, i32, C.POINTER(C.c_uint32)]),
     ("pa_spec_accept", i32, [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]),

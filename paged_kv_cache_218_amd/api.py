@@ -208,6 +208,13 @@ def pa_attention(desc: AttnDesc, q, k_pool, v_pool, block_tables, context_lens, 
                             _stream(stream)), "pa_attention")
 
 
+def pa_attention_noalloc(desc: AttnDesc, q, k_pool, v_pool, block_tables, context_lens, q_len: int,
+                         scale: float, out, stream=None) -> None:
+    _check(lib.pa_attention_noalloc(C.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                    _ptr(context_lens), q_len, scale, _ptr(out), _stream(stream)),
+           "pa_attention_noalloc")
+
+
 def pa_attention_tree(desc: AttnDesc, q, k_pool, v_pool, block_tables, context_lens, q_len: int,
                       tree_mask, mask_stride: int, scale: float, out, workspace=None, stream=None) -> None:
     """tree_mask: device uint32 masks, [B][mask_stride] or [q_len] when mask_stride is 0

@@ -60,6 +60,16 @@
 
 #include "pa_internal.h"
 
+// Scratch of the entry point that allocates nothing (pa_attention_noalloc):
+// one array per device, held until the process ends. Its first
+// kScratchCounterBytes hold the balanced schedule's arrival counters (cleared
+// by every call that uses them), the rest the partials. In host code
+// `scratch` only names the symbol: its device address comes from
+// scratch_base().
+constexpr size_t kScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+constexpr size_t kScratchCounterBytes = size_t(256) << 10;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace pa {
 namespace {
 thread_local int g_last_hip_error = 0;
@@ -1707,11 +1717,45 @@ extern "C" size_t pa_attention_workspace_size(const pa_attn_desc* desc, int32_t 
 
 namespace {
 
+// This device's copy of `scratch`, looked up once per device (with that
+// device current), or null with the HIP error recorded.
+void* scratch_base() {
+  static std::mutex mu;
+  static void* base[kMaxDevices];
+  int dev = 0;
+  if (const hipError_t e = hipGetDevice(&dev); e != hipSuccess) {
+    (void)hipGetLastError();
+    pa::hip_failed(e);
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!base[dev]) {
+    void* p = nullptr;
+    if (const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      pa::hip_failed(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return nullptr;
+    }
+    base[dev] = p;
+  }
+  return base[dev];
+}
+
+__global__ __launch_bounds__(256) void zero_words(int32_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0;
+}
+
+// Where the split-KV state of a call lives: the caller's workspace, or this
+// library's scratch.
+enum class Ws { caller, scratch };
+
 pa_status attention_impl(const pa_attn_desc* desc, const void* q, const void* k_pool,
                          const void* v_pool, const int32_t* block_tables,
                          const int32_t* context_lens, int32_t q_len, const uint32_t* tree_mask,
                          int32_t mask_stride, float scale, void* out, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         size_t workspace_bytes, Ws ws_kind, void* stream) {
   Plan pl;
   pa_status st = make_plan(desc, q_len, &pl);
   if (st != PA_OK) return st;
@@ -1719,8 +1763,21 @@ pa_status attention_impl(const pa_attn_desc* desc, const void* q, const void* k_
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
     return PA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
-  if (pl.ws > 0 && (!workspace || workspace_bytes < pl.ws)) return PA_ERR_INVALID_ARG;
-  if (pl.ws > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return PA_ERR_INVALID_ARG;  // 16-byte partial stores
+  char* counters_at = nullptr;  // arrival counters (balanced schedule)
+  char* partials_at = nullptr;  // (m, l) partials; o follows at pl.ws_o_off
+  if (ws_kind == Ws::caller) {
+    if (pl.ws > 0 && (!workspace || workspace_bytes < pl.ws)) return PA_ERR_INVALID_ARG;
+    if (pl.ws > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return PA_ERR_INVALID_ARG;  // 16-byte partial stores
+    counters_at = static_cast<char*>(workspace);
+    partials_at = counters_at + pl.ws_counters;
+  } else if (pl.ws > 0) {
+    if (pl.ws_counters > kScratchCounterBytes || pl.ws_partials > kScratchBytes - kScratchCounterBytes)
+      return PA_ERR_TOO_LARGE;
+    char* base = static_cast<char*>(scratch_base());
+    if (!base) return PA_ERR_HIP;
+    counters_at = base;
+    partials_at = base + kScratchCounterBytes;
+  }
   AttnArgs args;
   args.q = q;
   args.k_pool = k_pool;
@@ -1742,10 +1799,9 @@ pa_status attention_impl(const pa_attn_desc* desc, const void* q, const void* k_
     args.v_scales = reinterpret_cast<const float*>(static_cast<const char*>(v_pool) + codes);
   }
   if (pl.ws) {
-    char* w = static_cast<char*>(workspace);
-    if (pl.sched == PA_SCHED_BALANCED) args.counters = reinterpret_cast<int32_t*>(w);
-    args.part_ml = reinterpret_cast<float*>(w + pl.ws_counters);
-    args.part_o = reinterpret_cast<float*>(w + pl.ws_counters + pl.ws_o_off);
+    if (pl.sched == PA_SCHED_BALANCED) args.counters = reinterpret_cast<int32_t*>(counters_at);
+    args.part_ml = reinterpret_cast<float*>(partials_at);
+    args.part_o = reinterpret_cast<float*>(partials_at + pl.ws_o_off);
   }
   args.num_seqs = desc->num_seqs;
   args.hq = desc->num_q_heads;
@@ -1759,6 +1815,13 @@ pa_status attention_impl(const pa_attn_desc* desc, const void* q, const void* k_
   args.part_tokens = pl.part_tokens;
   args.scale_log2 = scale * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ws_kind == Ws::scratch && pl.sched == PA_SCHED_BALANCED) {
+    // the scratch's counters start every call at zero (a fill kernel, not a
+    // memset node, so that a captured graph replays it correctly)
+    hipLaunchKernelGGL(zero_words, dim3(std::min<int64_t>(64, (pl.segments + 255) / 256)), dim3(256), 0, s,
+                       args.counters, int64_t(pl.segments));
+    if (const hipError_t e = hipGetLastError(); e != hipSuccess) return pa::hip_failed(e);
+  }
   st = launch_main(pl, desc, args, s);
   if (st != PA_OK || pl.merge_grid == 0) return st;
   return desc->head_dim == 64 ? launch_merge<64>(pl, desc->dtype, args, s)
@@ -1773,7 +1836,15 @@ extern "C" pa_status pa_attention(const pa_attn_desc* desc, const void* q, const
                                   void* out, void* workspace, size_t workspace_bytes,
                                   void* stream) {
   return attention_impl(desc, q, k_pool, v_pool, block_tables, context_lens, q_len, nullptr, 0,
-                        scale, out, workspace, workspace_bytes, stream);
+                        scale, out, workspace, workspace_bytes, Ws::caller, stream);
+}
+
+extern "C" pa_status pa_attention_noalloc(const pa_attn_desc* desc, const void* q, const void* k_pool,
+                                          const void* v_pool, const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t q_len, float scale,
+                                          void* out, void* stream) {
+  return attention_impl(desc, q, k_pool, v_pool, block_tables, context_lens, q_len, nullptr, 0,
+                        scale, out, nullptr, 0, Ws::scratch, stream);
 }
 
 extern "C" pa_status pa_attention_tree(const pa_attn_desc* desc, const void* q, const void* k_pool,
@@ -1786,5 +1857,5 @@ extern "C" pa_status pa_attention_tree(const pa_attn_desc* desc, const void* q, 
   if (mask_stride != 0 && mask_stride < q_len) return PA_ERR_INVALID_ARG;
   if (desc && int64_t(mask_stride) * (desc->num_seqs - 1) + q_len > INT32_MAX) return PA_ERR_INVALID_ARG;
   return attention_impl(desc, q, k_pool, v_pool, block_tables, context_lens, q_len, tree_mask,
-                        mask_stride, scale, out, workspace, workspace_bytes, stream);
+                        mask_stride, scale, out, workspace, workspace_bytes, Ws::caller, stream);
 }

@@ -27,6 +27,7 @@ extern "C" const char* pa_status_string(pa_status s) {
     case PA_ERR_BAD_BLOCK: return "bad block (free block or refcount underflow)";
     case PA_ERR_HIP: return "HIP runtime error";
     case PA_ERR_NO_MEMORY: return "out of host memory";
+    case PA_ERR_TOO_LARGE: return "needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }

@@ -31,7 +31,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert pa.pa_status_string(s) != "unknown status"
     assert pa.pa_status_string(_lib.PA_ERR_NO_MEMORY) == "out of host memory"
     assert pa.pa_status_string(99) == "unknown status"
@@ -337,6 +337,27 @@ def test_attention_rejects_small_or_misaligned_workspace_before_launch():
     assert call(4096 + 8, size) == _lib.PA_ERR_INVALID_ARG      # 8-byte aligned only
     assert _lib.lib.pa_attention(C.byref(desc), fake, fake, fake, fake, fake, 1, float("nan"), fake, 4096,
                                  size, None) == _lib.PA_ERR_INVALID_ARG
+
+
+def test_noalloc_refuses_more_than_its_scratch_before_device_work():
+    """pa_attention_noalloc holds PA_NOALLOC_SCRATCH_BYTES of scratch; a call
+    whose split-KV state needs more is refused with PA_ERR_TOO_LARGE, and bad
+    arguments as pa_attention refuses them, all before any device work (the
+    pointers below are never dereferenced)."""
+    import ctypes as C
+    fake = 256
+    # 64 x 64 rows, 2,048 partitions of 64 tokens: 4,096 x 2,048 x 130 x 4 B of partials
+    big = pa.make_desc(64, 64, 8, 128, 32, 4096, 16384, pa.PA_DTYPE_BF16, 131072, partition_tokens=64)
+    assert pa.pa_attention_workspace_size(big, 1) > _lib.PA_NOALLOC_SCRATCH_BYTES
+    call = lambda d, scale=1.0: _lib.lib.pa_attention_noalloc(C.byref(d), fake, fake, fake, fake, fake, 1, scale,
+                                                              fake, None)
+    assert call(big) == _lib.PA_ERR_TOO_LARGE
+    assert pa.pa_status_string(_lib.PA_ERR_TOO_LARGE).startswith("needs more scratch")
+    assert call(big, float("nan")) == _lib.PA_ERR_INVALID_ARG
+    bad = pa.make_desc(64, 60, 8, 128, 32, 4096, 16384, pa.PA_DTYPE_BF16, 131072)   # 60 % 8 != 0
+    assert call(bad) == _lib.PA_ERR_INVALID_ARG
+    assert _lib.lib.pa_attention_noalloc(C.byref(big), None, fake, fake, fake, fake, 1, 1.0, fake,
+                                         None) == _lib.PA_ERR_INVALID_ARG
 
 
 def test_one_hip_runtime_per_process():
