@@ -93,6 +93,9 @@ constexpr int kMaxPartitions = 1 << 16;  // partitions per sequence
 constexpr int kMfmaMaxRows = 32;       // two 16-row tiles
 constexpr int kValuMaxRows = 16;
 constexpr float kLog2e = 1.4426950408889634f;
+// Lazy online-softmax rescaling: how far (base 2) a row's scores may exceed
+// its reference maximum before the reference moves; weights stay <= 2^8.
+constexpr float kLazyRescale = 8.f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -437,6 +440,20 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     s.s1 = s.ok ? int64_t(blk1) * a.hkv + g : 0;
     return s;
   };
+  // The accumulator rescale of the online softmax, skipped (a wave-uniform
+  // branch) in steps where no row's reference maximum moved.
+  auto rescale = [&](const float (&alpha)[NT]) {
+    bool moved = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) moved |= alpha[nt] != 1.f;
+    if (__ballot(moved) != 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) st.acc[nt][dt] *= alpha[nt];
+    }
+  };
+
   // Both step loops below keep one K and one V buffer per wave and refill
   // each with the next step's loads as soon as the current step has consumed
   // it: the next K right after the score MFMAs, the next V during P.V. A wave
@@ -538,9 +555,15 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
           }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(st.m[nt], mx);
+        // Lazy rescaling: the row's reference maximum m moves only when a
+        // score exceeds it by more than kLazyRescale (base 2), so weights
+        // stay below 2^kLazyRescale and the accumulator is rescaled only in
+        // the rare steps where some row's maximum jumps (the result does not
+        // depend on which reference is used: l and o are scaled alike).
+        const bool grow = mx > st.m[nt] + kLazyRescale;
+        const float m_new = grow ? mx : st.m[nt];
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        alpha[nt] = fast_exp2(st.m[nt] - m_use);
+        alpha[nt] = grow ? fast_exp2(st.m[nt] - m_use) : 1.f;
         st.m[nt] = m_new;
         uint32_t pk_hi[4], pk_lo[4];
         float psum = 0.f;
@@ -570,6 +593,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
 #pragma unroll
       for (int w4 = 0; w4 < 4; ++w4)
         keep[w4] = (2 * w4 + 1 < valid) ? 0xffffffffu : (2 * w4 < valid ? 0x0000ffffu : 0u);
+      rescale(alpha);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const uint32_t w0 = buf.v[dt][0], w1 = buf.v[dt][1];
@@ -577,7 +601,6 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
                            fp8x2_to_bf16x2<false>(w1) & keep[2], fp8x2_to_bf16x2<true>(w1) & keep[3]};
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          st.acc[nt][dt] *= alpha[nt];
           st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop),
                                                                    __builtin_bit_cast(bf16x8, pop_hi[nt]),
                                                                    st.acc[nt][dt], 0, 0, 0);
@@ -671,9 +694,15 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
           }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(st.m[nt], mx);
+        // Lazy rescaling: the row's reference maximum m moves only when a
+        // score exceeds it by more than kLazyRescale (base 2), so weights
+        // stay below 2^kLazyRescale and the accumulator is rescaled only in
+        // the rare steps where some row's maximum jumps (the result does not
+        // depend on which reference is used: l and o are scaled alike).
+        const bool grow = mx > st.m[nt] + kLazyRescale;
+        const float m_new = grow ? mx : st.m[nt];
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        alpha[nt] = fast_exp2(st.m[nt] - m_use);
+        alpha[nt] = grow ? fast_exp2(st.m[nt] - m_use) : 1.f;
         st.m[nt] = m_new;
         uint32_t pk[4];
         float psum = 0.f;
@@ -703,13 +732,13 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
 #pragma unroll
       for (int w4 = 0; w4 < 4; ++w4)
         keep[w4] = (2 * w4 + 1 < valid) ? 0xffffffffu : (2 * w4 < valid ? 0x0000ffffu : 0u);
+      rescale(alpha);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const u32x4 vm = {buf.v[dt][0] & keep[0], buf.v[dt][1] & keep[1], buf.v[dt][2] & keep[2],
                           buf.v[dt][3] & keep[3]};
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          st.acc[nt][dt] *= alpha[nt];
           st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vm),
                                                                    __builtin_bit_cast(bf16x8, pop[nt]),
                                                                    st.acc[nt][dt], 0, 0, 0);
