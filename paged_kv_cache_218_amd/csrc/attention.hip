@@ -120,6 +120,7 @@ struct AttnArgs {
   int32_t mask_stride;        // masks between consecutive sequences (0: one set for all)
   int32_t num_seqs, hq, hkv, group, mb, nb, q_len, max_ctx, parts, part_tokens;
   float scale_log2;  // scale * log2(e)
+  int32_t seg_cost;  // balanced: what starting a segment costs, in steps, when ranges are cut
 };
 
 __device__ __forceinline__ float bf16_to_f(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
@@ -934,6 +935,10 @@ __device__ __forceinline__ int64_t owner(int64_t x, int64_t S, int64_t N) {
 }
 
 constexpr int kMergeBatch = 8;   // pieces whose partial loads a thread has in flight at once
+// What a workgroup spends on a segment beyond its steps (the first step's
+// loads in flight, and at its end parking, combining and storing the rows)
+// is counted as work by the balanced partition, in steps (Plan::seg_cost),
+// so that ranges holding many short segments get fewer steps.
 constexpr int kMinGroupSteps = 8;  // fewest steps a workgroup's range holds
 
 // The workgroup that completed a segment merges its npieces partials, which
@@ -1006,9 +1011,11 @@ __global__ __launch_bounds__(64 * balanced_waves(NT)) void mfma_attn_balanced(At
     const int T = blockDim.x, tid = threadIdx.x;
     const int chunk = (B + T - 1) / T;
     const int b0 = min(B, tid * chunk), b1 = min(B, b0 + chunk);
+    // work units of each of the sequence's segments: its steps plus the
+    // cost of starting it (0 for an out-of-range length)
     auto steps_of = [&](int b) {
       const int L = a.lens[b];
-      return (L < a.q_len || L > a.max_ctx) ? 0 : (L + kStep - 1) / kStep;
+      return (L < a.q_len || L > a.max_ctx) ? 0 : (L + kStep - 1) / kStep + a.seg_cost;
     };
     int local = 0;
     for (int b = b0; b < b1; ++b) local += steps_of(b);
@@ -1060,14 +1067,20 @@ __global__ __launch_bounds__(64 * balanced_waves(NT)) void mfma_attn_balanced(At
   __shared__ int n_duty;
   if (threadIdx.x == 0) n_duty = 0;
   __syncthreads();
+  // A segment occupies seg_cost units for its start, then one unit per
+  // step; a range holds the steps of the units it covers (possibly none of
+  // a segment whose start units it ends in).
   int64_t x = x0;
   while (x < x1) {
-    int nb = pre[b + 1] - pre[b];
-    if (nb == 0 || int64_t(pre[b + 1]) * a.hkv <= x) { ++b; continue; }
+    const int nu = pre[b + 1] - pre[b];  // units of each segment of sequence b
+    if (nu == 0 || int64_t(pre[b + 1]) * a.hkv <= x) { ++b; continue; }
     const int64_t seq_start = int64_t(pre[b]) * a.hkv;
-    const int g = int((x - seq_start) / nb);
-    const int64_t seg_start = seq_start + int64_t(g) * nb, seg_end = seg_start + nb;
-    const int first = int(x - seg_start), last = int(min(x1, seg_end) - seg_start);
+    const int g = int((x - seq_start) / nu);
+    const int64_t seg_start = seq_start + int64_t(g) * nu, seg_end = seg_start + nu;
+    const int64_t real_start = seg_start + a.seg_cost;  // unit of the segment's first step
+    const int nb = nu - a.seg_cost;
+    if (min(x1, seg_end) <= real_start) { x = min(x1, seg_end); continue; }  // only start units here
+    const int first = int(max(x, real_start) - real_start), last = int(min(x1, seg_end) - real_start);
     const int L = a.lens[b];
     WaveState<D, NT> st;
     wave_state_init(st);
@@ -1109,7 +1122,7 @@ __global__ __launch_bounds__(64 * balanced_waves(NT)) void mfma_attn_balanced(At
       // partials after seeing their increments, and merges.
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      const int64_t k_first = owner(seg_start, S, N), k_last = owner(seg_end - 1, S, N);
+      const int64_t k_first = owner(real_start, S, N), k_last = owner(seg_end - 1, S, N);
       const int npieces = int(k_last - k_first + 1);
       __shared__ int arrived;
       if (threadIdx.x == 0)
@@ -1123,7 +1136,7 @@ __global__ __launch_bounds__(64 * balanced_waves(NT)) void mfma_attn_balanced(At
       }
     }
     __syncthreads();  // the park area is reused by the next piece
-    x = seg_start + last;
+    x = real_start + last;
   }
   // Merges after the steps (only a range's first and last piece can be
   // partial, so at most two), kept out of the step loop's registers.
@@ -1447,6 +1460,7 @@ struct Plan {
   bool kv8;     // FP8 pools
   bool tree;    // per-row visibility masks over the drafted positions
   int64_t segments, pieces;  // balanced schedule: segments, partial slots
+  int seg_cost;              // balanced schedule: a segment start's cost in steps
   // Workspace layout, the same for every schedule: the balanced schedule's
   // arrival counters (ws_counters bytes, reserved by every layout so that no
   // other schedule ever writes them), then the partials: (m, l) pairs at
@@ -1462,7 +1476,7 @@ int ceil_div(int64_t x, int64_t y) { return int((x + y - 1) / y); }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS of one compute unit (gfx950)
-constexpr int kPerCuMinContext = 6144;  // one workgroup per CU once the longest context reaches this
+constexpr int kPerCuMinContext = 2048;  // one workgroup per CU once the longest context reaches this
 
 size_t lds_bytes(const Plan& pl, int D, int num_seqs) {
   if (pl.path == PA_PATH_MFMA) {
@@ -1476,17 +1490,26 @@ size_t lds_bytes(const Plan& pl, int D, int num_seqs) {
   return std::max(first, merge) * sizeof(float);
 }
 
-// Default wavefronts per workgroup. Balanced schedule with long contexts:
-// one workgroup per compute unit holding every resident wave, so the
-// compute unit's waves share one range (workgroups dispatched earlier on a
-// compute unit otherwise run ahead of the later ones and finish early). With
-// shorter contexts the ranges hold more segment boundaries, where all of a
-// workgroup's waves wait for its slowest one, and three workgroups of four
-// waves per compute unit keep each other's gaps filled.
+// Default wavefronts per workgroup. Balanced schedule: one workgroup per
+// compute unit holding every resident wave, so the compute unit's waves
+// share one range (workgroups dispatched earlier on a compute unit otherwise
+// run ahead of the later ones and finish early), except where measurement
+// favours smaller ones: contexts shorter than kPerCuMinContext tokens (many
+// segment boundaries, where all of a workgroup's waves wait for its slowest
+// one) and the FP8 two-tile step (its conversions and split weights keep two
+// workgroups of four waves busier than one of eight).
 int default_waves(const Plan& pl, int max_context) {
-  if (pl.sched == PA_SCHED_BALANCED && pl.nt == 1 && max_context >= kPerCuMinContext)
-    return balanced_waves(pl.nt);
-  return 4;
+  if (pl.sched != PA_SCHED_BALANCED || max_context < kPerCuMinContext) return 4;
+  if (pl.nt == 2 && pl.kv8) return 4;
+  return balanced_waves(pl.nt);
+}
+
+// Cost of starting a segment in the balanced partition, in steps (measured
+// optimum per step kind: boundaries weigh more against the cheaper two-tile
+// steps of eight-wave workgroups).
+int default_segment_cost(const Plan& pl) {
+  if (pl.nt == 1) return pl.kv8 ? 16 : 8;
+  return pl.kv8 ? 16 : 32;
 }
 
 // Compute units of the current device, queried once per device and kept
@@ -1575,6 +1598,7 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
     pl->merge_grid = 0;
     pl->segments = pairs;
     pl->pieces = grid_max + pairs;
+    pl->seg_cost = default_segment_cost(*pl);
     pl->ws_counters = align256(size_t(pairs) * sizeof(int32_t));
     pl->ws_o_off = align256(size_t(pl->pieces) * rows * 2 * sizeof(float));
     pl->ws_partials = pl->ws_o_off + size_t(pl->pieces) * rows * d->head_dim * sizeof(float);
@@ -1843,6 +1867,7 @@ pa_status attention_impl(const pa_attn_desc* desc, const void* q, const void* k_
   args.parts = pl.parts;
   args.part_tokens = pl.part_tokens;
   args.scale_log2 = scale * kLog2e;
+  args.seg_cost = pl.sched == PA_SCHED_BALANCED ? pl.seg_cost : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ws_kind == Ws::scratch && pl.sched == PA_SCHED_BALANCED) {
     // the scratch's counters start every call at zero (a fill kernel, not a

@@ -215,12 +215,17 @@ def test_attention_plan_validation():
     pl = pa.pa_attention_plan(pa.make_desc(**ok), 1)
     assert pl.path == pa.PA_PATH_MFMA and pl.schedule == _lib.PA_SCHED_BALANCED
     assert pl.waves_per_group == 4 and pl.tiles_per_wave == 1
-    # long contexts: one workgroup per compute unit holding every resident wave (3 per SIMD)
-    long_ctx = {**ok, "max_context": 8192, "max_blocks_per_seq": 512}
+    # contexts of 2048 tokens or more: one workgroup per compute unit holding every resident
+    # wave (3 per SIMD with one row tile, 2 with two), except two FP8 tiles (two workgroups of 4)
+    long_ctx = {**ok, "max_context": 2048, "max_blocks_per_seq": 512}
     pl_long = pa.pa_attention_plan(pa.make_desc(**long_ctx), 1)
     assert pl_long.waves_per_group == 12 and pl_long.tiles_per_wave == 1
     pl_long = pa.pa_attention_plan(pa.make_desc(**{**long_ctx, "num_q_heads": 40}), 1)
+    assert pl_long.waves_per_group == 8 and pl_long.tiles_per_wave == 2
+    pl_long = pa.pa_attention_plan(pa.make_desc(**{**long_ctx, "num_q_heads": 40,
+                                                  "kv_format": pa.PA_KV_FP8_E4M3}), 1)
     assert pl_long.waves_per_group == 4 and pl_long.tiles_per_wave == 2
+    assert pa.pa_attention_plan(pa.make_desc(**{**long_ctx, "max_context": 2047}), 1).waves_per_group == 4
     assert pa.pa_attention_plan(pa.make_desc(**{**long_ctx, "num_q_heads": 40, "waves_per_group": 8}),
                                 1).waves_per_group == 8
     # 8 waves' park area for 32 rows plus 8192 sequences' step sums exceed the LDS
