@@ -817,23 +817,39 @@ __device__ bool park_states(const WaveState<D, NT>& st, int R, float* smem) {
   return __syncthreads_or(st.poisoned ? 1 : 0) != 0;
 }
 
-// Combine the W parked states of row r, column c: (M, l, o/l).
-__device__ __forceinline__ void combine_waves(const float* smem, int W, int R, int D, int r, int c,
-                                              float& M, float& l, float& o) {
-  const float* m_s = smem;
+// Combine the W parked wave states of a piece (log-sum-exp identity) in two
+// passes: per-row weights first (one thread per row: M = max_w m_w, l = sum_w 2^(m_w - M) l_w, and
+// weight_w = 2^(m_w - M) / l into wt [R][W]; M and l into row_ml [R][2]),
+// then any 4-column chunk of a row is sum_w weight_w o_w (park_chunk). Ends
+// with a barrier, after which every thread may read wt and row_ml.
+__device__ void park_row_weights(const float* park, int W, int R, float* wt, float* row_ml) {
+  const float* m_s = park;
   const float* l_s = m_s + W * R;
-  const float* o_s = l_s + W * R;
-  M = -INFINITY;
-  for (int w = 0; w < W; ++w) M = fmaxf(M, m_s[w * R + r]);
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-  l = 0.f;
-  float acc = 0.f;
-  for (int w = 0; w < W; ++w) {
-    const float f = fast_exp2(m_s[w * R + r] - Mu);
-    l += f * l_s[w * R + r];
-    acc += f * o_s[(w * R + r) * D + c];
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    float M = -INFINITY;
+    for (int w = 0; w < W; ++w) M = fmaxf(M, m_s[w * R + r]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float l = 0.f;
+    for (int w = 0; w < W; ++w) {
+      const float f = fast_exp2(m_s[w * R + r] - Mu);
+      wt[r * W + w] = f;
+      l += f * l_s[w * R + r];
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    for (int w = 0; w < W; ++w) wt[r * W + w] *= inv;
+    row_ml[2 * r] = M;
+    row_ml[2 * r + 1] = l;
   }
-  o = l > 0.f ? acc / l : 0.f;
+  __syncthreads();
+}
+
+// Columns c..c+3 of row r of the parked states combined (o = acc / l).
+__device__ __forceinline__ f32x4 park_chunk(const float* park, int W, int R, int D, const float* wt, int r, int c) {
+  const float* o_s = park + 2 * W * R;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int w = 0; w < W; ++w)
+    acc += wt[r * W + w] * *reinterpret_cast<const f32x4*>(o_s + (w * R + r) * D + c);
+  return acc;
 }
 
 // Fixed partitions: workgroup = (sequence, KV head, partition); partitions
@@ -1090,12 +1106,15 @@ __global__ __launch_bounds__(64 * balanced_waves(NT)) void mfma_attn_balanced(At
     const int64_t seg = int64_t(b) * a.hkv + g;
     const bool whole = first == 0 && last == nb;
     uint16_t* out = static_cast<uint16_t*>(a.out);
-    if (whole) {
-      for (int e = threadIdx.x; e < R * D; e += blockDim.x) {
-        const int r = e / D, c = e % D;
-        float M, l, o;
-        combine_waves(park, W, R, D, r, c, M, l, o);
-        store_f<uint16_t>(out + int64_t(out_row(a, b, g, r)) * D + c, bad ? NAN : o);
+    __shared__ float wt[kMfmaMaxRows * 16], row_ml[kMfmaMaxRows * 2];  // per-row wave weights, (M, l)
+    park_row_weights(park, W, R, wt, row_ml);
+    if (whole) {  // the rows, 4 columns (8 bytes) per store
+      for (int e = threadIdx.x; e < R * D / 4; e += blockDim.x) {
+        const int r = e / (D / 4), c = 4 * (e % (D / 4));
+        const f32x4 o = park_chunk(park, W, R, D, wt, r, c);
+        const u32x2 packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        *reinterpret_cast<u32x2*>(out + int64_t(out_row(a, b, g, r)) * D + c) =
+            bad ? (u32x2){0x7fc07fc0u, 0x7fc07fc0u} : packed;
       }
     } else {
       const int64_t piece = k + seg;
@@ -1104,17 +1123,11 @@ __global__ __launch_bounds__(64 * balanced_waves(NT)) void mfma_attn_balanced(At
       const auto o_r = partial_rsrc(a.part_o + piece * R * D, uint32_t(R) * D * 4);
       for (int e = threadIdx.x; e < R * D / 4; e += blockDim.x) {
         const int r = e / (D / 4), c = 4 * (e % (D / 4));
-        f32x4 v;
-        float M, l;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          float o;
-          combine_waves(park, W, R, D, r, c + u, M, l, o);
-          v[u] = o;
-        }
+        f32x4 v = park_chunk(park, W, R, D, wt, r, c);
         if (bad) v = (f32x4){NAN, NAN, NAN, NAN};
         store4_coherent(o_r, uint32_t(r * D + c) * 4, v);
-        if (c == 0) store2_coherent(ml_r, uint32_t(r) * 8, bad ? (f32x2){NAN, NAN} : (f32x2){M, l});
+        if (c == 0)
+          store2_coherent(ml_r, uint32_t(r) * 8, bad ? (f32x2){NAN, NAN} : (f32x2){row_ml[2 * r], row_ml[2 * r + 1]});
       }
       // Every wave waits until its partial stores are complete at the
       // coherent level, then one thread counts the piece in. The workgroup
@@ -1476,6 +1489,7 @@ int ceil_div(int64_t x, int64_t y) { return int((x + y - 1) / y); }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS of one compute unit (gfx950)
+constexpr size_t kStaticLdsReserve = 4096;    // the kernels' fixed __shared__ arrays
 constexpr int kPerCuMinContext = 2048;  // one workgroup per CU once the longest context reaches this
 
 size_t lds_bytes(const Plan& pl, int D, int num_seqs) {
@@ -1583,7 +1597,7 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   const int max_waves = balanced ? balanced_waves(pl->nt) : 4;
   if (d->waves_per_group > max_waves) return PA_ERR_UNSUPPORTED;
   pl->waves = d->waves_per_group ? d->waves_per_group : default_waves(*pl, d->max_context);
-  while (lds_bytes(*pl, d->head_dim, d->num_seqs) > kMaxLdsBytes) {
+  while (lds_bytes(*pl, d->head_dim, d->num_seqs) > kMaxLdsBytes - kStaticLdsReserve) {
     if (d->waves_per_group || pl->waves == 1) return PA_ERR_UNSUPPORTED;
     pl->waves = pl->waves > 4 ? 4 : pl->waves / 2;
   }
