@@ -302,50 +302,52 @@ def attention_flops(cfg, lens, tree_parents=None) -> int:
 
 def read_probe(gib: int = 4, reps: int = 10):
     """Practical HBM read ceilings: the library's read probe over a `gib` GiB
-    buffer read once per call as 8 KiB blocks, over a few launch shapes, in
-    two orders: a seeded random permutation (the attention kernels' access
-    pattern: each (block, KV head) slice is one 8 KiB block somewhere in the
-    pool) and ascending (a contiguous streaming read). The best random-order
-    rate is the ceiling the attention kernels are compared with; the
-    streaming rate, and that of random 64 KiB runs, say what the random order
-    of 8 KiB slices costs."""
+    buffer read once per call, over a few launch shapes, in four orders: a
+    seeded random permutation of 8 KiB blocks (the attention kernels' access
+    pattern at block size 32: each (block, KV head) slice is one 8 KiB block
+    somewhere in the pool), the same of 4 KiB blocks (block size 16), random
+    64 KiB runs (eight adjacent 8 KiB blocks) and ascending 8 KiB blocks (a
+    contiguous streaming read). The best random-order rate at the slice size
+    of a workload is the ceiling its attention kernel is compared with; the
+    streaming rate says what the random order of slices costs."""
     import torch
     import paged_kv_cache_218_amd as pa
-    n_blocks = gib * 2**30 // 8192
-    buf = torch.ones(n_blocks * 8192, dtype=torch.uint8, device="cuda")
+    nbytes = gib * 2**30
+    n_blocks = nbytes // 8192
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     gen = torch.Generator().manual_seed(218)
     runs = torch.randperm(n_blocks // 8, generator=gen).to(torch.int32)
-    orders = {"random": torch.randperm(n_blocks, generator=gen).to(torch.int32).cuda(),
+    orders = {"random": (8192, torch.randperm(n_blocks, generator=gen).to(torch.int32).cuda()),
+              "random_4k": (4096, torch.randperm(2 * n_blocks, generator=gen).to(torch.int32).cuda()),
               # 64 KiB runs (eight adjacent 8 KiB blocks, e.g. every KV head of one pool block) in random order
-              "random_64k_runs": (runs[:, None] * 8 + torch.arange(8, dtype=torch.int32)).reshape(-1).cuda(),
-              "sequential": torch.arange(n_blocks, dtype=torch.int32, device="cuda")}
+              "random_64k_runs": (8192, (runs[:, None] * 8 + torch.arange(8, dtype=torch.int32)).reshape(-1).cuda()),
+              "sequential": (8192, torch.arange(n_blocks, dtype=torch.int32, device="cuda"))}
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     rows = []
-    for name, order in orders.items():
+    for name, (block_bytes, order) in orders.items():
         for depth in (1, 2, 4):
             for waves_per_cu in (8, 16, 32):
                 wgs = 256 * waves_per_cu // 4
                 for _ in range(2):
-                    pa.pa_read_probe(buf, order, depth, wgs, sink)
+                    pa.pa_read_probe(buf, order, depth, wgs, sink, block_bytes=block_bytes)
                 torch.cuda.synchronize()
                 e0.record()
                 for _ in range(reps):
-                    pa.pa_read_probe(buf, order, depth, wgs, sink)
+                    pa.pa_read_probe(buf, order, depth, wgs, sink, block_bytes=block_bytes)
                 e1.record()
                 torch.cuda.synchronize()
                 us = e0.elapsed_time(e1) / reps * 1e3
-                rows.append({"order": name, "blocks_in_flight": depth, "workgroups": wgs, "us": round(us, 1),
-                             "gbs": round(n_blocks * 8192 / us / 1e3, 1)})
-                log(f"read probe ({name}): {depth} blocks in flight per wave, {wgs} workgroups: {us:.1f} us, "
-                    f"{rows[-1]['gbs']} GB/s")
-    best = max((r for r in rows if r["order"] == "random"), key=lambda r: r["gbs"])
-    best_seq = max((r for r in rows if r["order"] == "sequential"), key=lambda r: r["gbs"])
-    best_64k = max((r for r in rows if r["order"] == "random_64k_runs"), key=lambda r: r["gbs"])
-    return {"bytes": n_blocks * 8192, "order": "seeded random permutation of 8 KiB blocks",
-            "best_gbs": best["gbs"], "best_frac_of_8tbs": round(best["gbs"] / 8000, 4),
-            "random_64k_runs_best_gbs": best_64k["gbs"],
-            "sequential_best_gbs": best_seq["gbs"], "sequential_best_frac_of_8tbs": round(best_seq["gbs"] / 8000, 4),
+                rows.append({"order": name, "block_bytes": block_bytes, "blocks_in_flight": depth,
+                             "workgroups": wgs, "us": round(us, 1), "gbs": round(nbytes / us / 1e3, 1)})
+                log(f"read probe ({name}, {block_bytes} B blocks): {depth} blocks in flight per wave, "
+                    f"{wgs} workgroups: {us:.1f} us, {rows[-1]['gbs']} GB/s")
+    best = {name: max((r for r in rows if r["order"] == name), key=lambda r: r["gbs"])["gbs"] for name in orders}
+    return {"bytes": nbytes, "order": "seeded random permutation of 8 KiB blocks",
+            "best_gbs": best["random"], "best_frac_of_8tbs": round(best["random"] / 8000, 4),
+            "random_4k_best_gbs": best["random_4k"], "random_4k_best_frac_of_8tbs": round(best["random_4k"] / 8000, 4),
+            "random_64k_runs_best_gbs": best["random_64k_runs"],
+            "sequential_best_gbs": best["sequential"], "sequential_best_frac_of_8tbs": round(best["sequential"] / 8000, 4),
             "runs": rows}
 
 
@@ -502,7 +504,7 @@ def main():
                     help="after the timed region, time this many calls on the CPU side (0: skip)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--read-probe", action="store_true",
-                    help="measure the device's read ceiling (8 KiB blocks in random order) and exit")
+                    help="measure the device's read ceilings (4 and 8 KiB blocks in random order, streaming) and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--bench-json", help="with --pmc-summary: a bench line of the workload (data-dependent bytes); "

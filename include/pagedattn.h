@@ -497,9 +497,11 @@ pa_status pa_tree_masks(const int32_t* parents, int32_t n, uint32_t* masks);
 
 /* Read-bandwidth probe, a measurement aid for the HBM roofline of the
  * attention kernels (not part of the attention path): reads num_blocks
- * blocks of 8 KiB of `buf` in the order given, the access pattern of a
+ * blocks of block_bytes of `buf` in the order given, the access pattern of a
  * pool's (block, KV head) slices, with non-temporal loads.
- *   buf               device, >= num_blocks * 8192 bytes
+ *   buf               device, >= num_blocks * block_bytes bytes
+ *   block_bytes       4096 or 8192 (a slice at block size 16 or 32, head
+ *                     dimension 128, bf16)
  *   order             device int32 [num_blocks]: block ids to read (a
  *                     permutation for a full pass; ids outside
  *                     [0, num_blocks) are clamped, never read past buf)
@@ -510,7 +512,7 @@ pa_status pa_tree_masks(const int32_t* parents, int32_t n, uint32_t* masks);
  * Asynchronous on `stream`; time it with events around the call.
  * PA_ERR_INVALID_ARG for null pointers or bad sizes, PA_ERR_HIP if the launch
  * fails. */
-pa_status pa_read_probe(const void* buf, int64_t num_blocks, const int32_t* order,
+pa_status pa_read_probe(const void* buf, int64_t num_blocks, int32_t block_bytes, const int32_t* order,
                         int32_t blocks_in_flight, int32_t workgroups, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus

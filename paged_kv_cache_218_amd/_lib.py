@@ -68,7 +68,7 @@ SIGNATURES = [
     ("pa_prefix_evict", i32, [vp, i32, pi32, pi32]),
     ("pa_prefix_cache_stats", i32, [vp, pi32, pi32, pi32]),
     ("pa_prefix_cache_dump", i32, [vp, pi32, pi32, C.POINTER(i64), i32, pi32]),
-    ("pa_read_probe", i32, [vp, i64, vp, i32, i32, vp, vp]),
+    ("pa_read_probe", i32, [vp, i64, i32, vp, i32, i32, vp, vp]),
     ("pa_last_hip_error", i32, []),
     ("pa_hip_error_name", C.c_char_p, [i32]),
 ]

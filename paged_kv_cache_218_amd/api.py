@@ -252,12 +252,13 @@ def pa_spec_accept(p, q, draft, u_accept, u_draw, num_accepted, tokens, workspac
 
 # -- measurement aid -----------------------------------------------------------
 
-def pa_read_probe(buf, order, blocks_in_flight: int, workgroups: int, sink, stream=None) -> None:
-    """Read the device tensor `buf` (>= order.numel() * 8192 bytes) as 8 KiB
-    blocks in the order of the int32 device tensor `order`; sink: int32/uint32
-    device tensor of one element."""
-    _check(lib.pa_read_probe(_ptr(buf), int(order.numel()), _ptr(order), blocks_in_flight, workgroups,
-                             _ptr(sink), _stream(stream)), "pa_read_probe")
+def pa_read_probe(buf, order, blocks_in_flight: int, workgroups: int, sink, stream=None,
+                  block_bytes: int = 8192) -> None:
+    """Read the device tensor `buf` (>= order.numel() * block_bytes bytes) as
+    blocks of block_bytes (4096 or 8192) in the order of the int32 device
+    tensor `order`; sink: int32/uint32 device tensor of one element."""
+    _check(lib.pa_read_probe(_ptr(buf), int(order.numel()), int(block_bytes), _ptr(order), blocks_in_flight,
+                             workgroups, _ptr(sink), _stream(stream)), "pa_read_probe")
 
 
 # -- radix prefix cache -------------------------------------------------------

@@ -310,6 +310,16 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w), 1.0f, HIGH));
 }
 
+// Maximum over the four lanes n, n+16, n+32, n+48 of a wavefront (the lanes
+// holding one MFMA row), returned in all four: two lane-swap steps between
+// 16-lane rows and between 32-lane halves, VALU work with no LDS round trip.
+__device__ __forceinline__ float row_max4(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 template <int D>
 struct StepBuf {
   u32x4 k[2][D / 32];  // two 16-token K tiles, D/32 k-steps each
@@ -554,8 +564,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
             s2[e] = v;
             mx = fmaxf(mx, v);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = row_max4(mx);
         // Lazy rescaling: the row's reference maximum m moves only when a
         // score exceeds it by more than kLazyRescale (base 2), so weights
         // stay below 2^kLazyRescale and the accumulator is rescaled only in
@@ -693,8 +702,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
             s2[4 * i + r] = v;
             mx = fmaxf(mx, v);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = row_max4(mx);
         // Lazy rescaling: the row's reference maximum m moves only when a
         // score exceeds it by more than kLazyRescale (base 2), so weights
         // stay below 2^kLazyRescale and the accumulator is rescaled only in

@@ -399,9 +399,10 @@ def test_spec_accept_rejects_bad_arguments_before_launch():
 def test_read_probe_rejects_bad_arguments_before_launch():
     fake = 256
     call = lambda *a: _lib.lib.pa_read_probe(*a)
-    for args in [(None, 4, fake, 1, 8, fake, None), (fake, 4, None, 1, 8, fake, None),
-                 (fake, 4, fake, 1, 8, None, None), (fake, 0, fake, 1, 8, fake, None),
-                 (fake, 4, fake, 1, 0, fake, None), (fake, 4, fake, 3, 8, fake, None)]:
+    for args in [(None, 4, 8192, fake, 1, 8, fake, None), (fake, 4, 8192, None, 1, 8, fake, None),
+                 (fake, 4, 8192, fake, 1, 8, None, None), (fake, 0, 8192, fake, 1, 8, fake, None),
+                 (fake, 4, 8192, fake, 1, 0, fake, None), (fake, 4, 8192, fake, 3, 8, fake, None),
+                 (fake, 4, 2048, fake, 1, 8, fake, None), (fake, 4, 8193, fake, 1, 8, fake, None)]:
         assert call(*args) == _lib.PA_ERR_INVALID_ARG, args
 
 

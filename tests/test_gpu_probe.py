@@ -13,9 +13,10 @@ def test_read_probe_passes():
     buf = torch.ones(n * 8192, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     order = torch.randperm(n, generator=torch.Generator().manual_seed(3)).to(torch.int32).cuda()
-    for depth in (1, 2, 4):
-        pa.pa_read_probe(buf, order, depth, 8, sink)
     bad = torch.tensor([0, n, -1, 2 ** 30] * (n // 4), dtype=torch.int32, device="cuda")
-    pa.pa_read_probe(buf, bad, 2, 4, sink)
+    for block_bytes in (4096, 8192):
+        for depth in (1, 2, 4):
+            pa.pa_read_probe(buf, order, depth, 8, sink, block_bytes=block_bytes)
+        pa.pa_read_probe(buf, bad, 2, 4, sink, block_bytes=block_bytes)
     torch.cuda.synchronize()
     assert int(sink.item()) == 0
