@@ -58,9 +58,11 @@
  *               then scales [num_blocks][num_kv_heads][block_size]
  *       v_pool: codes [num_blocks][num_kv_heads][head_dim][block_size],
  *               then scales [num_blocks][num_kv_heads][block_size]
- *     Rows are written as bf16 and quantised per (token, KV head):
- *     scale = max|x| / 448 (1 for an all-zero row), code = round-to-nearest-
- *     even(x / scale), both in fp32.
+ *     Rows are written as bf16 and quantised per (token, KV head): scale =
+ *     the smallest power of two >= max|x| / 448 (the quotient in fp32; 1 for
+ *     an all-zero row), code = round-to-nearest-even(x / scale) in fp32 (the
+ *     division is exact). Power-of-two scales keep every weight times its
+ *     token's V scale a bf16 number, so attention applies them exactly.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H

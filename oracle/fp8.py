@@ -8,9 +8,13 @@ the scale granularity; the readings taken here:
     bits; exponent 0 is subnormal (m * 2^-9); S.1111.111 is NaN; no infinity;
     largest finite 448;
   * rounding: to nearest, ties to even, on the fp32 value;
-  * scales: one fp32 scale per (token, KV head), scale = amax / 448 over that
-    token's head vector (1 for an all-zero vector), code = round(x / scale),
-    both operations in fp32. The dequantised value is decode(code) * scale.
+  * scales: one fp32 scale per (token, KV head): the smallest power of two
+    that is >= amax / 448 over that token's head vector (the quotient taken in
+    fp32; 1 for an all-zero vector), code = round(x / scale) (exact division
+    by a power of two, then the rounding above). The dequantised value is
+    decode(code) * scale. A power-of-two scale (like the shared exponents of
+    the OCP microscaling formats) changes no code's relative precision, and a
+    weight times it stays a bf16 number, so attention applies it exactly.
 """
 from __future__ import annotations
 
@@ -68,11 +72,19 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     return (code | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
 
 
+def pow2_ceil(s: np.ndarray) -> np.ndarray:
+    """The smallest power of two >= s, elementwise, for fp32 s > 0."""
+    s = np.asarray(s, dtype=np.float32)
+    frac, e = np.frexp(s.astype(np.float64))  # s = frac * 2^e, frac in [0.5, 1)
+    return np.where(frac == 0.5, s.astype(np.float64), np.ldexp(1.0, e)).astype(np.float32)
+
+
 def quantize_rows(x: np.ndarray):
     """Quantise the last axis of fp32 x: returns (codes uint8 like x, scales fp32 x.shape[:-1])."""
     x = np.asarray(x, dtype=np.float32)
     amax = np.abs(x).max(axis=-1)
-    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    scale = np.where(amax > 0, pow2_ceil(np.where(amax > 0, q, np.float32(1.0))), np.float32(1.0)).astype(np.float32)
     y = (x / scale[..., None]).astype(np.float32)
     return e4m3_encode(y), scale
 

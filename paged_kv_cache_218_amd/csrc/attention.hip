@@ -542,12 +542,13 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
           for (int r = 0; r < 4; ++r) sc[nt][i][r] *= buf.ks[i][r];
         }
     };
-    // Online softmax. Each token's V scale multiplies its weight in P.V (not
-    // in the row sum). The scaled weight w is not a bf16 number, so it enters
-    // P.V as w_hi + w_lo, two bf16 parts (residual ~2^-17 relative): one
-    // dominant token would otherwise carry w's 2^-9 rounding into the row.
-    auto softmax8 = [&](const f32x4 (&sc)[NT][2], const StepBuf8<D>& buf, int tb, u32x4 (&pop_hi)[NT],
-                        u32x4 (&pop_lo)[NT], float (&alpha)[NT]) {
+    // Online softmax. Each weight is rounded to bf16 once (the row sum adds
+    // the rounded weights, so the output stays a convex combination of the
+    // dequantised V rows); its token's V scale, a power of two, then
+    // multiplies it exactly, so P.V takes the scaled weights as bf16 numbers
+    // with no further rounding.
+    auto softmax8 = [&](const f32x4 (&sc)[NT][2], const StepBuf8<D>& buf, int tb, u32x4 (&pop)[NT],
+                        float (&alpha)[NT]) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         float s2[8];
@@ -575,27 +576,27 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         alpha[nt] = grow ? fast_exp2(st.m[nt] - m_use) : 1.f;
         st.m[nt] = m_new;
-        uint32_t pk_hi[4], pk_lo[4];
+        uint32_t pk[4];
         float psum = 0.f;
 #pragma unroll
         for (int w4 = 0; w4 < 4; ++w4) {
           const int e0 = 2 * w4, e1 = 2 * w4 + 1;
-          const float p0 = fast_exp2(s2[e0] - m_use), p1 = fast_exp2(s2[e1] - m_use);
+          const uint32_t pr = pack_bf16x2(fast_exp2(s2[e0] - m_use), fast_exp2(s2[e1] - m_use));
+          const float p0 = __uint_as_float(pr << 16), p1 = __uint_as_float(pr & 0xffff0000u);
           psum += p0 + p1;
+          // masked tokens: the select keeps a scale past the context (any
+          // bits) out of the weight
           const float q0 = vis[e0] ? p0 * buf.vs[e0 / 4][e0 % 4] : 0.f;
           const float q1 = vis[e1] ? p1 * buf.vs[e1 / 4][e1 % 4] : 0.f;
-          const uint32_t hi = pack_bf16x2(q0, q1);
-          pk_hi[w4] = hi;
-          pk_lo[w4] = pack_bf16x2(q0 - __uint_as_float(hi << 16), q1 - __uint_as_float(hi & 0xffff0000u));
+          pk[w4] = pack_bf16x2(q0, q1);
         }
         st.l[nt] = st.l[nt] * alpha[nt] + psum;
-        pop_hi[nt] = (u32x4){pk_hi[0], pk_hi[1], pk_hi[2], pk_hi[3]};
-        pop_lo[nt] = (u32x4){pk_lo[0], pk_lo[1], pk_lo[2], pk_lo[3]};
+        pop[nt] = (u32x4){pk[0], pk[1], pk[2], pk[3]};
       }
     };
     // P.V of one step (the step's only use of the V codes).
-    auto accumulate8 = [&](const StepBuf8<D>& buf, int tb, const u32x4 (&pop_hi)[NT],
-                           const u32x4 (&pop_lo)[NT], const float (&alpha)[NT], bool last) {
+    auto accumulate8 = [&](const StepBuf8<D>& buf, int tb, const u32x4 (&pop)[NT], const float (&alpha)[NT],
+                           bool last) {
       // tokens past the context hold the NaN code: zeroed by a select on the
       // wave's last step, the only one that can hold the sequence's tail
       const int valid = last ? min(max(L - (tb + 8 * j), 0), 8) : 8;
@@ -610,14 +611,10 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
         const u32x4 vop = {fp8x2_to_bf16x2<false>(w0) & keep[0], fp8x2_to_bf16x2<true>(w0) & keep[1],
                            fp8x2_to_bf16x2<false>(w1) & keep[2], fp8x2_to_bf16x2<true>(w1) & keep[3]};
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int nt = 0; nt < NT; ++nt)
           st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop),
-                                                                   __builtin_bit_cast(bf16x8, pop_hi[nt]),
+                                                                   __builtin_bit_cast(bf16x8, pop[nt]),
                                                                    st.acc[nt][dt], 0, 0, 0);
-          st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop),
-                                                                   __builtin_bit_cast(bf16x8, pop_lo[nt]),
-                                                                   st.acc[nt][dt], 0, 0, 0);
-        }
       }
     };
     StepBuf8<D> buf;
@@ -627,24 +624,24 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     for (int sn = next_step(first); sn < end; sn = next_step(sn)) {
       const StepLoc nxt = locate(sn);
       f32x4 sc[NT][2];
-      u32x4 hi[NT], lo[NT];
+      u32x4 pop[NT];
       float alpha[NT];
       qk8(buf, sc);
       __builtin_amdgcn_sched_barrier(0);
       load_k8(buf, nxt);
       __builtin_amdgcn_sched_barrier(0);
-      softmax8(sc, buf, cur.tb, hi, lo, alpha);
-      accumulate8(buf, cur.tb, hi, lo, alpha, false);
+      softmax8(sc, buf, cur.tb, pop, alpha);
+      accumulate8(buf, cur.tb, pop, alpha, false);
       load_v8(buf, nxt);
       st.poisoned |= !cur.ok;
       cur = nxt;
     }
     f32x4 sc[NT][2];
-    u32x4 hi[NT], lo[NT];
+    u32x4 pop[NT];
     float alpha[NT];
     qk8(buf, sc);
-    softmax8(sc, buf, cur.tb, hi, lo, alpha);
-    accumulate8(buf, cur.tb, hi, lo, alpha, true);
+    softmax8(sc, buf, cur.tb, pop, alpha);
+    accumulate8(buf, cur.tb, pop, alpha, true);
     st.poisoned |= !cur.ok;
   } else {
     const int64_t head_stride = int64_t(BS) * D;  // elements of one (block, head) slice

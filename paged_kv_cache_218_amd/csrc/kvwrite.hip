@@ -66,10 +66,20 @@ __global__ void scatter_kernel(T* __restrict__ k_pool, T* __restrict__ v_pool,
 
 // FP8 pools: quantise while scattering. A group of d/8 lanes holds one
 // (token, KV head) row, 8 bf16 elements per lane; the group's max |x| sets
-// scale = amax / 448 (1 for an all-zero row) and each element becomes the
-// E4M3 code of x / scale (round to nearest even, v_cvt_pk_fp8_f32). Lanes
-// past the end still take part in the group shuffles but store nothing.
+// the scale, the smallest power of two >= amax / 448 (1 for an all-zero
+// row), and each element becomes the E4M3 code of x / scale (exact: a power
+// of two; then round to nearest even, v_cvt_pk_fp8_f32). Lanes past the end
+// still take part in the group shuffles but store nothing.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// The smallest power of two >= s, for finite s > 0 (subnormals included).
+__device__ __forceinline__ float pow2_ceil(float s) {
+  const uint32_t b = __float_as_uint(s);
+  const uint32_t m = b & 0x7fffffu;
+  if (m == 0) return s;                                                   // 2^e already
+  if (b >= 0x800000u) return __uint_as_float((b & 0x7f800000u) + 0x800000u);  // the next binade
+  return __uint_as_float(1u << (32 - __clz(m - 1)));  // subnormal: m units of 2^-149
+}
 
 __device__ __forceinline__ float bf16_bits_to_f(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -112,8 +122,8 @@ __global__ void scatter_fp8_kernel(uint8_t* __restrict__ k_codes, uint8_t* __res
     vmax = fmaxf(vmax, __shfl_xor(vmax, o));
   }
   if (!live) return;
-  const float ks = kmax > 0.f ? kmax / 448.f : 1.f;
-  const float vs = vmax > 0.f ? vmax / 448.f : 1.f;
+  const float ks = kmax > 0.f ? pow2_ceil(kmax / 448.f) : 1.f;
+  const float vs = vmax > 0.f ? pow2_ceil(vmax / 448.f) : 1.f;
   uint32_t kc[2], vc[2];
 #pragma unroll
   for (int w = 0; w < 2; ++w) {

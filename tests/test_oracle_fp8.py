@@ -44,15 +44,39 @@ def test_quantize_rows_properties():
     x[5] = 0.0
     codes, scales = fp8.quantize_rows(x)
     assert codes[5].max() == 0 and scales[5] == 1.0
-    # the largest magnitude of each row lands exactly on +-448
+    # every scale is a power of two, the smallest one with amax / scale <= 448
+    frac, _ = np.frexp(scales.astype(np.float64))
+    assert (frac == 0.5).all()
+    live = np.arange(300) != 5
+    amax = np.abs(x).max(axis=1).astype(np.float64)
+    ratio = amax[live] / scales[live]
+    assert (ratio <= 448.0 * (1 + 2.0 ** -23)).all() and (ratio > 224.0 * (1 - 2.0 ** -23)).all()
+    # so the largest magnitude of each row takes one of the codes for (224, 448]
     amax_idx = np.abs(x).argmax(axis=1)
     top = codes[np.arange(300), amax_idx] & 0x7F
-    assert (top[np.arange(300) != 5] == 0x7E).all()
+    assert ((top[live] >= 0x76) & (top[live] <= 0x7E)).all()
     deq = fp8.dequantize(codes, scales)
     # within half a unit in the last place: 2^-4 relative for normals, 2^-10 * scale near zero
     bound = np.maximum(np.abs(x) * 2.0 ** -4, scales[:, None].astype(np.float64) * 2.0 ** -10)
     assert (np.abs(deq - x) <= bound * (1 + 1e-12)).all()
     assert not np.array_equal(deq, x)
+
+
+def test_pow2_ceil_is_the_smallest_power_of_two_not_below():
+    rng = np.random.default_rng(9)
+    # normal and subnormal fp32 values, exact powers of two and their neighbours
+    s = np.concatenate([
+        (rng.uniform(0.5, 1.0, 4000) * 2.0 ** rng.integers(-140, 100, 4000)).astype(np.float32),
+        np.float32(2.0) ** np.arange(-149, 100, dtype=np.float64).astype(np.float32),
+        np.nextafter(np.float32(2.0) ** np.arange(-148, 100).astype(np.float32), np.float32(np.inf)),
+        np.nextafter(np.float32(2.0) ** np.arange(-148, 100).astype(np.float32), np.float32(0)),
+    ]).astype(np.float32)
+    s = s[s > 0]
+    got = fp8.pow2_ceil(s).astype(np.float64)
+    # brute force: the first of 2^-149, 2^-148, ... that is >= s
+    powers = 2.0 ** np.arange(-149, 128, dtype=np.float64)
+    want = powers[np.searchsorted(powers, s.astype(np.float64), side="left")]
+    assert np.array_equal(got, want)
 
 
 @pytest.mark.parametrize("name,kw", [
@@ -69,8 +93,9 @@ def test_fp8_pool_attention_vs_torch_sdpa(name, kw):
         # dequantise with torch's own float8 decode and the oracle-independent scales
         kq = torch.from_numpy(to_f64(k, "bf16").astype(np.float32))
         vq = torch.from_numpy(to_f64(v, "bf16").astype(np.float32))
-        ks = kq.abs().amax(-1, keepdim=True) / 448.0
-        vs = vq.abs().amax(-1, keepdim=True) / 448.0
+        # scales: the power of two 2^ceil(log2(amax / 448)), the quotient in fp32, the log in fp64
+        ks = torch.exp2(torch.ceil(torch.log2((kq.abs().amax(-1, keepdim=True) / 448.0).double()))).float()
+        vs = torch.exp2(torch.ceil(torch.log2((vq.abs().amax(-1, keepdim=True) / 448.0).double()))).float()
         kd = (kq / ks).to(torch.float8_e4m3fn).double() * ks.double()
         vd = (vq / vs).to(torch.float8_e4m3fn).double() * vs.double()
         ref = torch_sdpa_seq(w.seqs[b].q, kd.numpy(), vd.numpy(), cfg.q_len, cfg.group, cfg.scale, "bf16",
