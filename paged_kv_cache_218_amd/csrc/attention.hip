@@ -57,6 +57,7 @@
 #include <cmath>
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "pa_internal.h"
 
@@ -515,6 +516,8 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     // Scores of every row tile, each times its token's K scale (exact: the
     // scale multiplies the dot product): the step's only use of K.
     auto qk8 = [&](const StepBuf8<D>& buf, f32x4 (&sc)[NT][2]) {
+      // each token's K scale times scale * log2(e): the scores come out in base 2
+      const f32x4 ks[2] = {buf.ks[0] * a.scale_log2, buf.ks[1] * a.scale_log2};
       // codes -> bf16 (exact); K: slab sl gives k-steps 2sl (codes 0-7) and 2sl+1 (8-15)
       u32x4 kop[2][KS];
 #pragma unroll
@@ -539,7 +542,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
                                                                  sc[nt][i], 0, 0, 0);
           // e = 4i + r is token tb + 8j + e
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sc[nt][i][r] *= buf.ks[i][r];
+          for (int r = 0; r < 4; ++r) sc[nt][i][r] *= ks[i][r];
         }
     };
     // Online softmax. Each weight is rounded to bf16 once (the row sum adds
@@ -547,21 +550,23 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     // dequantised V rows); its token's V scale, a power of two, then
     // multiplies it exactly, so P.V takes the scaled weights as bf16 numbers
     // with no further rounding.
-    auto softmax8 = [&](const f32x4 (&sc)[NT][2], const StepBuf8<D>& buf, int tb, u32x4 (&pop)[NT],
+    // FULL: a step every row sees whole (no masking work).
+    auto softmax8 = [&](auto FULL, const f32x4 (&sc)[NT][2], const StepBuf8<D>& buf, int tb, u32x4 (&pop)[NT],
                         float (&alpha)[NT]) {
+      constexpr bool kFull = decltype(FULL)::value;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         float s2[8];
         bool vis[8];
         float mx = -INFINITY;
-        const uint32_t tbits = TREE ? tree_bits(tb, nt) : 0u;
+        const uint32_t tbits = (TREE && !kFull) ? tree_bits(tb, nt) : 0u;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int e = 4 * i + r;
-            vis[e] = visible(tb + 8 * j + e, nt, tbits, e);
-            const float v = vis[e] ? sc[nt][i][r] * a.scale_log2 : -INFINITY;
+            vis[e] = kFull || visible(tb + 8 * j + e, nt, tbits, e);
+            const float v = vis[e] ? sc[nt][i][r] : -INFINITY;  // K scales carry scale * log2(e)
             s2[e] = v;
             mx = fmaxf(mx, v);
           }
@@ -630,7 +635,8 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
       __builtin_amdgcn_sched_barrier(0);
       load_k8(buf, nxt);
       __builtin_amdgcn_sched_barrier(0);
-      softmax8(sc, buf, cur.tb, pop, alpha);
+      if (cur.tb + kStep <= ctx_end) softmax8(std::true_type{}, sc, buf, cur.tb, pop, alpha);
+      else softmax8(std::false_type{}, sc, buf, cur.tb, pop, alpha);
       accumulate8(buf, cur.tb, pop, alpha, false);
       load_v8(buf, nxt);
       st.poisoned |= !cur.ok;
@@ -640,7 +646,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     u32x4 pop[NT];
     float alpha[NT];
     qk8(buf, sc);
-    softmax8(sc, buf, cur.tb, pop, alpha);
+    softmax8(std::false_type{}, sc, buf, cur.tb, pop, alpha);
     accumulate8(buf, cur.tb, pop, alpha, true);
     st.poisoned |= !cur.ok;
   } else {
@@ -683,18 +689,20 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     };
     // Online softmax of the scores: leaves the bf16 probabilities and the
     // rescale factors for P.V.
-    auto softmax = [&](const f32x4 (&sc)[NT][2], int tb, u32x4 (&pop)[NT], float (&alpha)[NT]) {
+    // FULL: a step every row sees whole (no masking work).
+    auto softmax = [&](auto FULL, const f32x4 (&sc)[NT][2], int tb, u32x4 (&pop)[NT], float (&alpha)[NT]) {
+      constexpr bool kFull = decltype(FULL)::value;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         // mask and scale; e = 4*i + r is token tb + 8j + e
         float s2[8];
         float mx = -INFINITY;
-        const uint32_t tbits = TREE ? tree_bits(tb, nt) : 0u;
+        const uint32_t tbits = (TREE && !kFull) ? tree_bits(tb, nt) : 0u;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const bool vis = visible(tb + 8 * j + 4 * i + r, nt, tbits, 4 * i + r);
+            const bool vis = kFull || visible(tb + 8 * j + 4 * i + r, nt, tbits, 4 * i + r);
             const float v = vis ? sc[nt][i][r] * a.scale_log2 : -INFINITY;
             s2[4 * i + r] = v;
             mx = fmaxf(mx, v);
@@ -773,7 +781,8 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
       __builtin_amdgcn_sched_barrier(0);
       load_k(buf, nxt);
       __builtin_amdgcn_sched_barrier(0);
-      softmax(sc, cur.tb, pop, alpha);
+      if (cur.tb + kStep <= ctx_end) softmax(std::true_type{}, sc, cur.tb, pop, alpha);
+      else softmax(std::false_type{}, sc, cur.tb, pop, alpha);
       accumulate(buf, cur.tb, pop, alpha, false);
       load_v(buf, nxt);
       st.poisoned |= !cur.ok;
@@ -783,7 +792,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
     u32x4 pop[NT];
     float alpha[NT];
     qk(buf, sc);
-    softmax(sc, cur.tb, pop, alpha);
+    softmax(std::false_type{}, sc, cur.tb, pop, alpha);
     accumulate(buf, cur.tb, pop, alpha, true);
     st.poisoned |= !cur.ok;
   }
