@@ -529,7 +529,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sharding is described in DESIGN.md, not implemented)", file=sys.stderr)
+              "(the sharding design is written up, not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch
