@@ -1532,12 +1532,11 @@ int default_waves(const Plan& pl, int max_context) {
   return balanced_waves(pl.nt);
 }
 
-// Cost of starting a segment in the balanced partition, in steps (measured
-// optimum per step kind: boundaries weigh more against the cheaper two-tile
-// steps of eight-wave workgroups).
+// Cost of starting a segment in the balanced partition, in steps (the
+// measured optimum per pool format: an FP8 step moves half the bytes, so a
+// boundary weighs more steps).
 int default_segment_cost(const Plan& pl) {
-  if (pl.nt == 1) return pl.kv8 ? 16 : 8;
-  return pl.kv8 ? 16 : 32;
+  return pl.kv8 ? 16 : 12;
 }
 
 // Compute units of the current device, queried once per device and kept
