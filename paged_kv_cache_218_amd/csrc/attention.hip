@@ -122,6 +122,7 @@ struct AttnArgs {
   int32_t num_seqs, hq, hkv, group, mb, nb, q_len, max_ctx, parts, part_tokens;
   float scale_log2;  // scale * log2(e)
   int32_t seg_cost;  // balanced: what starting a segment costs, in steps, when ranges are cut
+  int32_t run_parts;  // one wavefront per partition: consecutive partitions per wavefront (>= 1)
 };
 
 __device__ __forceinline__ float bf16_to_f(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
@@ -362,9 +363,14 @@ __device__ __forceinline__ void wave_state_init(WaveState<D, NT>& st) {
 // sequence b (context L), KV head g. Every step covers 32 tokens; tokens at
 // or past L, and tokens after a row's causal limit, are masked.
 // next_step(s) gives the wave's step after s (>= end: none left).
-template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE, typename NextStep>
+// on_step(s) runs after every step s but the wave's last one (s < end - 1
+// steps of the same wave follow it), with the state holding step s.
+struct NoStepHook {
+  __device__ void operator()(int) const {}
+};
+template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE, typename NextStep, typename OnStep = NoStepHook>
 __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int first, int end,
-                                WaveState<D, NT>& st, NextStep next_step) {
+                                WaveState<D, NT>& st, NextStep next_step, OnStep on_step = {}) {
   constexpr int KS = D / 32;  // k-steps over the head dim for QK
   constexpr int DT = D / 16;  // 16-row tiles of the head dim for PV
   const int lane = threadIdx.x % 64;
@@ -640,6 +646,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
       accumulate8(buf, cur.tb, pop, alpha, false);
       load_v8(buf, nxt);
       st.poisoned |= !cur.ok;
+      on_step(cur.tb / kStep);
       cur = nxt;
     }
     f32x4 sc[NT][2];
@@ -786,6 +793,7 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
       accumulate(buf, cur.tb, pop, alpha, false);
       load_v(buf, nxt);
       st.poisoned |= !cur.ok;
+      on_step(cur.tb / kStep);
       cur = nxt;
     }
     f32x4 sc[NT][2];
@@ -892,56 +900,141 @@ __global__ __launch_bounds__(256, 2) void mfma_attn(AttnArgs a) {
 // step pipeline and writes the partition's (m, l, o = acc / l) partial, or
 // the final rows of a one-partition sequence, straight from its registers:
 // no LDS, no barrier. lse_merge combines the partials as for mfma_attn.
-template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE>
+//
+// Runs (run_parts > 1, when there are more partitions than wave slots):
+// each pair's partitions are cut into runs of run_parts consecutive ones
+// (the last run of a pair may be shorter), one wavefront per run, which
+// streams its run as one step sequence, so the step pipeline stays full
+// across partition boundaries (a partition's start would otherwise wait for its first loads,
+// and its end for its last). At each boundary the finished partition's
+// partial is parked in the wave's LDS slots (no global store inside the step
+// loop, whose load waits count exactly) and the state starts over; the
+// parked partials and the last one go to memory after the loop. Each
+// partition is still computed on its own: the same partials as one wavefront
+// per partition, bit for bit.
+template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE, bool RUNS>
 __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void mfma_attn_wave(AttnArgs a) {
+  extern __shared__ float smem[];  // runs: [W][run_parts - 1][R][D + 8] parked states
   const int W = blockDim.x / 64, wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int n = lane & 15, j = lane >> 4;
-  const int gpw = (a.parts + W - 1) / W;
-  const int pair = blockIdx.x / gpw;
-  const int part = (blockIdx.x % gpw) * W + wave;
-  if (part >= a.parts) return;
-  const int g = pair % a.hkv, b = pair / a.hkv;
-  const int L = a.lens[b];
   const int R = a.group * a.q_len;
   uint16_t* out = static_cast<uint16_t*>(a.out);
-  if (L < a.q_len || L > a.max_ctx) {  // NaN rows: here for one partition, else by the merge kernel
-    if (part == 0 && a.parts == 1)
-      for (int e = lane; e < R * D; e += 64)
-        store_f<uint16_t>(out + int64_t(out_row(a, b, g, e / D)) * D + e % D, NAN);
-    return;
-  }
-  const int t0 = part * a.part_tokens;
-  if (t0 >= L) return;  // past the sequence: the merge kernel reads only its partitions
-  const int t1 = min(t0 + a.part_tokens, L);
-  WaveState<D, NT> st;
-  wave_state_init(st);
-  mfma_wave_steps<D, BS, NT, STREAM, KV8, TREE>(a, b, g, L, t0 / kStep, (t1 + kStep - 1) / kStep, st,
-                                                [](int s) { return s + 1; });
-  const bool final_rows = L <= a.part_tokens;
+  // the partial of partition `part` of (b, g) from the state, or the final
+  // rows of a one-partition sequence
+  auto emit = [&](const WaveState<D, NT>& st, int b, int g, int part, bool final_rows) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float l = st.l[nt] + __shfl_xor(st.l[nt], 16);  // row sum: the 4 lanes of the row
-    l += __shfl_xor(l, 32);
-    const int r = nt * 16 + n;
-    if (r >= R) continue;
-    const int row = out_row(a, b, g, r);
-    const int64_t pi = int64_t(row) * a.parts + part;
+    for (int nt = 0; nt < NT; ++nt) {
+      float l = st.l[nt] + __shfl_xor(st.l[nt], 16);  // row sum: the 4 lanes of the row
+      l += __shfl_xor(l, 32);
+      const int r = nt * 16 + n;
+      if (r >= R) continue;
+      const int row = out_row(a, b, g, r);
+      const int64_t pi = int64_t(row) * a.parts + part;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      f32x4 o;
+      for (int dt = 0; dt < D / 16; ++dt) {
+        f32x4 o;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) o[k] = st.poisoned ? NAN : (l > 0.f ? st.acc[nt][dt][k] / l : 0.f);
-      const int c = 16 * dt + 4 * j;
-      if (final_rows) {
+        for (int k = 0; k < 4; ++k) o[k] = st.poisoned ? NAN : (l > 0.f ? st.acc[nt][dt][k] / l : 0.f);
+        const int c = 16 * dt + 4 * j;
+        if (final_rows) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) store_f<uint16_t>(out + int64_t(row) * D + c + k, o[k]);
-      } else {
-        *reinterpret_cast<f32x4*>(a.part_o + pi * D + c) = o;
+          for (int k = 0; k < 4; ++k) store_f<uint16_t>(out + int64_t(row) * D + c + k, o[k]);
+        } else {
+          *reinterpret_cast<f32x4*>(a.part_o + pi * D + c) = o;
+        }
+      }
+      if (!final_rows && j == 0) {
+        a.part_ml[pi * 2 + 0] = st.poisoned ? NAN : st.m[nt];
+        a.part_ml[pi * 2 + 1] = st.poisoned ? NAN : l;
       }
     }
-    if (!final_rows && j == 0) {
-      a.part_ml[pi * 2 + 0] = st.poisoned ? NAN : st.m[nt];
-      a.part_ml[pi * 2 + 1] = st.poisoned ? NAN : l;
+  };
+  if constexpr (!RUNS) {
+    const int gpw = (a.parts + W - 1) / W;
+    const int pair = blockIdx.x / gpw;
+    const int part = (blockIdx.x % gpw) * W + wave;
+    if (part >= a.parts) return;
+    const int g = pair % a.hkv, b = pair / a.hkv;
+    const int L = a.lens[b];
+    if (L < a.q_len || L > a.max_ctx) {  // NaN rows: here for one partition, else by the merge kernel
+      if (part == 0 && a.parts == 1)
+        for (int e = lane; e < R * D; e += 64)
+          store_f<uint16_t>(out + int64_t(out_row(a, b, g, e / D)) * D + e % D, NAN);
+      return;
+    }
+    const int t0 = part * a.part_tokens;
+    if (t0 >= L) return;  // past the sequence: the merge kernel reads only its partitions
+    const int t1 = min(t0 + a.part_tokens, L);
+    WaveState<D, NT> st;
+    wave_state_init(st);
+    mfma_wave_steps<D, BS, NT, STREAM, KV8, TREE>(a, b, g, L, t0 / kStep, (t1 + kStep - 1) / kStep, st,
+                                                  [](int s) { return s + 1; });
+    emit(st, b, g, part, L <= a.part_tokens);
+    return;
+  }
+  // runs (partials, or the final rows of a one-partition sequence). A parked
+  // partial keeps, per row, m, the 4 lanes' partial row sums, a poison flag
+  // and the raw accumulator; the flush forms l and o = acc / l exactly as
+  // emit does.
+  constexpr int kSlotRow = D + 8;  // floats per parked row (16-byte aligned)
+  const int spp = a.part_tokens / kStep;  // steps per partition
+  const int rpp = (a.parts + a.run_parts - 1) / a.run_parts;  // runs per pair
+  const int64_t wid = int64_t(blockIdx.x) * W + wave;
+  if (wid >= int64_t(a.num_seqs) * a.hkv * rpp) return;
+  const int pair = int(wid / rpp);
+  const int p0 = int(wid % rpp) * a.run_parts, p1 = min(a.parts, p0 + a.run_parts);  // partitions p0 .. p1 - 1
+  float* slots = smem + int64_t(wave) * (a.run_parts - 1) * R * kSlotRow;
+  {
+    const int g = pair % a.hkv, b = pair / a.hkv;
+    const int L = a.lens[b];
+    if (L < a.q_len || L > a.max_ctx) return;  // NaN rows: by the merge kernel
+    const int s0 = p0 * spp, s1 = min(p1 * spp, (L + kStep - 1) / kStep);
+    if (s0 >= s1) return;  // partitions past the sequence
+    WaveState<D, NT> st;
+    wave_state_init(st);
+    int parked = 0;
+    int part_end = s0 + spp - 1;  // the last step of the partition in progress
+    // a partition ends after step s: park its state, start the next one
+    auto boundary = [&](int s) {
+      if (s != part_end) return;
+      part_end += spp;
+      float* slot = slots + int64_t(parked) * R * kSlotRow;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int r = nt * 16 + n;
+        if (r >= R) continue;
+        float* dst = slot + r * kSlotRow;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(dst + 8 + 16 * dt + 4 * j) = st.acc[nt][dt];
+        dst[1 + j] = st.l[nt];
+        if (j == 0) {
+          dst[0] = st.m[nt];
+          dst[5] = st.poisoned ? 1.f : 0.f;
+        }
+      }
+      ++parked;
+      wave_state_init(st);
+    };
+    mfma_wave_steps<D, BS, NT, STREAM, KV8, TREE>(a, b, g, L, s0, s1, st, [](int s) { return s + 1; }, boundary);
+    emit(st, b, g, (s1 - 1) / spp, L <= a.part_tokens);  // a one-partition sequence: its final rows
+    for (int i = 0; i < parked; ++i) {  // the parked partials, partitions p0, p0 + 1, ...
+      const float* slot = slots + int64_t(i) * R * kSlotRow;
+      for (int e = lane; e < R * (D / 4); e += 64) {
+        const int r = e / (D / 4), c = 4 * (e % (D / 4));
+        const float* row = slot + r * kSlotRow;
+        const float l = (row[1] + row[2]) + (row[3] + row[4]);  // as emit sums the 4 lanes
+        const bool bad = row[5] != 0.f;
+        const f32x4 acc = *reinterpret_cast<const f32x4*>(row + 8 + c);
+        f32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = bad ? NAN : (l > 0.f ? acc[k] / l : 0.f);
+        const int64_t pi = int64_t(out_row(a, b, g, r)) * a.parts + p0 + i;
+        *reinterpret_cast<f32x4*>(a.part_o + pi * D + c) = o;
+        if (c == 0) {
+          a.part_ml[pi * 2 + 0] = bad ? NAN : row[0];
+          a.part_ml[pi * 2 + 1] = bad ? NAN : l;
+        }
+      }
     }
   }
 }
@@ -1488,6 +1581,7 @@ struct Plan {
   bool tree;    // per-row visibility masks over the drafted positions
   int64_t segments, pieces;  // balanced schedule: segments, partial slots
   int seg_cost;              // balanced schedule: a segment start's cost in steps
+  int run_parts = 1;         // one wavefront per partition: consecutive partitions per wavefront
   // Workspace layout, the same for every schedule: the balanced schedule's
   // arrival counters (ws_counters bytes, reserved by every layout so that no
   // other schedule ever writes them), then the partials: (m, l) pairs at
@@ -1509,7 +1603,9 @@ constexpr int kPerCuMinContext = 2048;  // one workgroup per CU once the longest
 size_t lds_bytes(const Plan& pl, int D, int num_seqs) {
   if (pl.path == PA_PATH_MFMA) {
     const size_t park = size_t(pl.waves) * pl.rows * (D + 2) * sizeof(float);
-    if (pl.sched == PA_SCHED_PARTITIONS_WAVE) return 0;
+    // runs: each wave's parked partials
+    if (pl.sched == PA_SCHED_PARTITIONS_WAVE)
+      return size_t(pl.waves) * (pl.run_parts - 1) * pl.rows * (D + 8) * sizeof(float);
     if (pl.sched == PA_SCHED_PARTITIONS) return park;
     return size_t((num_seqs + 1 + 3) & ~3) * sizeof(int32_t) + park;  // step prefix sums, then the park area
   }
@@ -1651,7 +1747,23 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   // partition without waiting for other waves and writes its partial from
   // registers; with fewer, the waves of a workgroup share a partition.
   if (path == PA_PATH_MFMA && pairs * parts >= int64_t(cus) * kWavesPerCu) pl->sched = PA_SCHED_PARTITIONS_WAVE;
-  const int64_t grid = pl->sched == PA_SCHED_PARTITIONS_WAVE ? pairs * ceil_div(parts, waves) : pairs * parts;
+  int64_t grid = pl->sched == PA_SCHED_PARTITIONS_WAVE ? pairs * ceil_div(parts, waves) : pairs * parts;
+  // More partitions than resident waves: runs of consecutive partitions per
+  // wave, so that every wave is resident from the start and its step
+  // pipeline runs on across partition boundaries. A run parks all but its
+  // last partial in LDS: the run is as long as full occupancy leaves room for.
+  pl->run_parts = 1;
+  if (pl->sched == PA_SCHED_PARTITIONS_WAVE && parts > 1 && pt % kStep == 0) {
+    const int per_cu = pl->nt == 1 ? kWavesPerCu : balanced_waves(2);
+    const int64_t total = pairs * parts;
+    const size_t slot = size_t(rows) * (d->head_dim + 8) * sizeof(float);
+    const int kmax = 1 + int((kMaxLdsBytes - kStaticLdsReserve) / (size_t(per_cu) * slot));
+    const int k = std::min<int64_t>(kmax, (total + int64_t(cus) * per_cu - 1) / (int64_t(cus) * per_cu));
+    if (k > 1) {
+      pl->run_parts = k;
+      grid = (pairs * ceil_div(parts, k) + waves - 1) / waves;
+    }
+  }
   if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
   pl->part_tokens = pt;
   pl->parts = parts;
@@ -1706,17 +1818,20 @@ int resident_groups(const void* kernel, int threads, size_t lds) {
   return per_cu * cus;
 }
 
-// The main kernel a plan launches (one template instance per shape).
+// The main kernel a plan launches (one template instance per shape; sched is
+// the plan's schedule, or kSchedRuns for one wavefront per partition in runs).
+constexpr int kSchedRuns = -1;
 template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE>
 const void* mfma_kernel(int sched) {
   if (sched == PA_SCHED_BALANCED) return reinterpret_cast<const void*>(mfma_attn_balanced<D, BS, NT, STREAM, KV8, TREE>);
-  if (sched == PA_SCHED_PARTITIONS_WAVE) return reinterpret_cast<const void*>(mfma_attn_wave<D, BS, NT, STREAM, KV8, TREE>);
+  if (sched == PA_SCHED_PARTITIONS_WAVE) return reinterpret_cast<const void*>(mfma_attn_wave<D, BS, NT, STREAM, KV8, TREE, false>);
+  if (sched == kSchedRuns) return reinterpret_cast<const void*>(mfma_attn_wave<D, BS, NT, STREAM, KV8, TREE, true>);
   return reinterpret_cast<const void*>(mfma_attn<D, BS, NT, STREAM, KV8, TREE>);
 }
 
 template <int D, int BS, int NT, bool TREE>
 const void* mfma_kernel(const Plan& pl) {
-  const int sc = pl.sched;
+  const int sc = pl.sched == PA_SCHED_PARTITIONS_WAVE && pl.run_parts > 1 ? kSchedRuns : pl.sched;
   if (pl.kv8)
     return pl.stream ? mfma_kernel<D, BS, NT, true, true, TREE>(sc) : mfma_kernel<D, BS, NT, false, true, TREE>(sc);
   return pl.stream ? mfma_kernel<D, BS, NT, true, false, TREE>(sc) : mfma_kernel<D, BS, NT, false, false, TREE>(sc);
@@ -1895,6 +2010,7 @@ pa_status attention_impl(const pa_attn_desc* desc, const void* q, const void* k_
   args.part_tokens = pl.part_tokens;
   args.scale_log2 = scale * kLog2e;
   args.seg_cost = pl.sched == PA_SCHED_BALANCED ? pl.seg_cost : 0;
+  args.run_parts = pl.run_parts;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ws_kind == Ws::scratch && pl.sched == PA_SCHED_BALANCED) {
     // the scratch's counters start every call at zero (a fill kernel, not a

@@ -239,15 +239,21 @@ def test_attention_plan_validation():
     assert pl.schedule == _lib.PA_SCHED_PARTITIONS and pl.num_partitions == 2
     pl = pa.pa_attention_plan(pa.make_desc(**{**ok, "path": pa.PA_PATH_VALU}), 1)
     assert pl.schedule == _lib.PA_SCHED_PARTITIONS
-    # partitions that fill the device's 3072 wave slots on their own: one wavefront each
+    # partitions that fill the device's 3072 wave slots on their own: one wavefront each,
+    # and with more partitions than slots (8,192 here) runs of 3 consecutive partitions per
+    # wavefront: ceil(256 / 3) = 86 runs per (sequence, KV head), 4 wavefronts per workgroup
     many = {**ok, "num_seqs": 4, "num_kv_heads": 8, "num_q_heads": 64, "block_size": 32,
             "max_context": 131072, "max_blocks_per_seq": 4096, "num_blocks": 16384, "partition_tokens": 512}
     pl = pa.pa_attention_plan(pa.make_desc(**many), 1)
     assert pl.schedule == _lib.PA_SCHED_PARTITIONS_WAVE and pl.num_partitions == 256
-    assert pl.grid == 32 * 256 // 4 and pl.merge_grid == 4 * 64
+    assert pl.grid == 32 * 86 // 4 and pl.merge_grid == 4 * 64
     rows_parts = 4 * 64 * 256
     # the balanced schedule's counter area (4 x 8 pairs, one 256-byte unit) comes first in every layout
     assert pl.workspace_bytes == 256 + -(-rows_parts * 8 // 256) * 256 + rows_parts * 128 * 4
+    # partitions that exactly fill the slots: one wavefront each
+    exact = {**many, "num_seqs": 3, "max_context": 65536, "max_blocks_per_seq": 2048}
+    pl = pa.pa_attention_plan(pa.make_desc(**exact), 1)  # 24 pairs x 128 partitions = 3072 slots
+    assert pl.schedule == _lib.PA_SCHED_PARTITIONS_WAVE and pl.grid == 24 * 128 // 4
     assert pa.pa_attention_plan(pa.make_desc(**{**many, "max_context": 3072 * 512 // 32 - 512}),
                                 1).schedule == _lib.PA_SCHED_PARTITIONS
     assert pa.pa_attention_plan(pa.make_desc(**{**many, "path": pa.PA_PATH_VALU}),

@@ -79,3 +79,32 @@ def test_per_wave_partitions_bad_lengths_and_tables_give_nan():
     ref = oracle_rows(w, good)
     for b in good:
         assert_close(o[b], ref[b], "bf16", f"seq {b}")
+
+
+def test_runs_bit_identical_to_one_partition_per_wave():
+    """With more partitions than wave slots, each wavefront streams a run of
+    consecutive partitions (parking the finished ones' states in LDS); every
+    partition is still computed on its own, so the rows equal, bit for bit,
+    those of a batch whose partitions exactly fill the wave slots (one
+    partition per wavefront), and match the oracle."""
+    import paged_kv_cache_218_amd as pa
+    from tests.gpu_util import out_bits
+    base = workloads.config("llama3_70b_decode", batch=4, len_const=0, lens=(8192, 8192 - 37, 8000, 8192))
+    w4 = workloads.generate(base)
+    w3 = workloads.generate(workloads.config("llama3_70b_decode", batch=3, len_const=0,
+                                             lens=(8192, 8192 - 37, 8000)))
+    out4, cache4 = run_gpu(w4, partition_tokens=PT)
+    out3, cache3 = run_gpu(w3, partition_tokens=PT)
+    p4, p3 = plan_of(cache4, w4, PT), plan_of(cache3, w3, PT)
+    assert p4.schedule == pa.PA_SCHED_PARTITIONS_WAVE
+    if p3.schedule != pa.PA_SCHED_PARTITIONS_WAVE or p3.grid != 3 * 8 * (8192 // PT) // p3.waves_per_group:
+        pytest.skip("the three-sequence batch does not exactly fill this device's wave slots")
+    assert p4.grid < 4 * 8 * (8192 // PT) // p4.waves_per_group  # runs: fewer wavefronts than partitions
+    # the two batches' sequences 0-2 are the same seeded data only if the generator draws them alike
+    assert np.array_equal(w4.q_all()[:3], w3.q_all())
+    b4, b3 = out_bits(out4), out_bits(out3)
+    assert np.array_equal(b4[:3], b3)
+    got = out_to_f64(out4, "bf16")
+    ref = oracle_rows(w4, range(4))
+    for b in range(4):
+        assert_close(got[b], ref[b], "bf16", f"runs seq {b}")
