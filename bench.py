@@ -102,6 +102,9 @@ def kernel_name(cfg, plan, desc) -> str:
     stream = "false" if desc.kv_shared else "true"
     kv8 = "true" if desc.kv_format else "false"
     tree = "true" if cfg.tree else "false"
+    if plan.schedule == 2:  # one wavefront per partition, or per run of partitions
+        runs = "true" if plan.partitions_per_wave > 1 else "false"
+        return f"{base}<{cfg.head_dim}, {cfg.block_size}, {nt}, {stream}, {kv8}, {tree}, {runs}>"
     return f"{base}<{cfg.head_dim}, {cfg.block_size}, {nt}, {stream}, {kv8}, {tree}>"
 
 
@@ -623,6 +626,7 @@ def main():
             "schedule": {0: "partitions", 1: "balanced", 2: "partitions_wave"}[plan.schedule], "kv_shared": int(desc.kv_shared),
             "partitions": plan.num_partitions, "waves_per_group": plan.waves_per_group,
             "grid": plan.grid, "merge_grid": plan.merge_grid, "tiles_per_wave": plan.tiles_per_wave,
+            "partitions_per_wave": plan.partitions_per_wave,
         },
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(tokens, 1),

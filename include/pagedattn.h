@@ -283,6 +283,10 @@ typedef struct pa_attn_plan {
   int32_t merge_grid;         /* workgroups of the merge kernel (0 if none) */
   int32_t tiles_per_wave;     /* MFMA: 16-row query tiles each wavefront holds (1, or 2
                                  when G*q_len > 16); 0 for the VALU path */
+  int32_t partitions_per_wave; /* PARTITIONS_WAVE: consecutive partitions of one (sequence,
+                                 KV head) each wavefront streams: 1, or a run of several
+                                 when the partitions outnumber the device's wave slots;
+                                 0 for the other schedules */
   size_t workspace_bytes;     /* workspace pa_attention needs */
 } pa_attn_plan;
 

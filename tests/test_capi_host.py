@@ -246,14 +246,14 @@ def test_attention_plan_validation():
             "max_context": 131072, "max_blocks_per_seq": 4096, "num_blocks": 16384, "partition_tokens": 512}
     pl = pa.pa_attention_plan(pa.make_desc(**many), 1)
     assert pl.schedule == _lib.PA_SCHED_PARTITIONS_WAVE and pl.num_partitions == 256
-    assert pl.grid == 32 * 86 // 4 and pl.merge_grid == 4 * 64
+    assert pl.grid == 32 * 86 // 4 and pl.merge_grid == 4 * 64 and pl.partitions_per_wave == 3
     rows_parts = 4 * 64 * 256
     # the balanced schedule's counter area (4 x 8 pairs, one 256-byte unit) comes first in every layout
     assert pl.workspace_bytes == 256 + -(-rows_parts * 8 // 256) * 256 + rows_parts * 128 * 4
     # partitions that exactly fill the slots: one wavefront each
     exact = {**many, "num_seqs": 3, "max_context": 65536, "max_blocks_per_seq": 2048}
     pl = pa.pa_attention_plan(pa.make_desc(**exact), 1)  # 24 pairs x 128 partitions = 3072 slots
-    assert pl.schedule == _lib.PA_SCHED_PARTITIONS_WAVE and pl.grid == 24 * 128 // 4
+    assert pl.schedule == _lib.PA_SCHED_PARTITIONS_WAVE and pl.grid == 24 * 128 // 4 and pl.partitions_per_wave == 1
     assert pa.pa_attention_plan(pa.make_desc(**{**many, "max_context": 3072 * 512 // 32 - 512}),
                                 1).schedule == _lib.PA_SCHED_PARTITIONS
     assert pa.pa_attention_plan(pa.make_desc(**{**many, "path": pa.PA_PATH_VALU}),
