@@ -363,8 +363,8 @@ __device__ __forceinline__ void wave_state_init(WaveState<D, NT>& st) {
 // sequence b (context L), KV head g. Every step covers 32 tokens; tokens at
 // or past L, and tokens after a row's causal limit, are masked.
 // next_step(s) gives the wave's step after s (>= end: none left).
-// on_step(s) runs after every step s but the wave's last one (s < end - 1
-// steps of the same wave follow it), with the state holding step s.
+// on_step(s) runs after each of the wave's steps except its last, once step
+// s is in the state (its loads for the next step already issued).
 struct NoStepHook {
   __device__ void operator()(int) const {}
 };
@@ -1614,18 +1614,19 @@ size_t lds_bytes(const Plan& pl, int D, int num_seqs) {
   return std::max(first, merge) * sizeof(float);
 }
 
-// Default wavefronts per workgroup. Balanced schedule: one workgroup per
-// compute unit holding every resident wave, so the compute unit's waves
-// share one range (workgroups dispatched earlier on a compute unit otherwise
-// run ahead of the later ones and finish early), except where measurement
-// favours smaller ones: contexts shorter than kPerCuMinContext tokens (many
-// segment boundaries, where all of a workgroup's waves wait for its slowest
-// one) and the FP8 two-tile step (its conversions and split weights keep two
-// workgroups of four waves busier than one of eight).
+// Default wavefronts per workgroup. Balanced schedule: one workgroup of 8
+// waves per compute unit, so the compute unit's waves share one range
+// (workgroups dispatched earlier on a compute unit otherwise run ahead of the
+// later ones and finish early); with one row tile the registers would allow
+// 12 resident waves, but 8 measure faster (the 70B layer by 1%), except where
+// measurement favours smaller workgroups: contexts shorter than
+// kPerCuMinContext tokens (many segment boundaries, where all of a
+// workgroup's waves wait for its slowest one) and the FP8 two-tile step (two
+// workgroups of four waves keep its conversions busier than one of eight).
 int default_waves(const Plan& pl, int max_context) {
   if (pl.sched != PA_SCHED_BALANCED || max_context < kPerCuMinContext) return 4;
   if (pl.nt == 2 && pl.kv8) return 4;
-  return balanced_waves(pl.nt);
+  return 8;
 }
 
 // Cost of starting a segment in the balanced partition, in steps (the

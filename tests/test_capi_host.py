@@ -215,11 +215,13 @@ def test_attention_plan_validation():
     pl = pa.pa_attention_plan(pa.make_desc(**ok), 1)
     assert pl.path == pa.PA_PATH_MFMA and pl.schedule == _lib.PA_SCHED_BALANCED
     assert pl.waves_per_group == 4 and pl.tiles_per_wave == 1
-    # contexts of 2048 tokens or more: one workgroup per compute unit holding every resident
-    # wave (3 per SIMD with one row tile, 2 with two), except two FP8 tiles (two workgroups of 4)
+    # contexts of 2048 tokens or more: one workgroup of 8 waves per compute unit (with one
+    # row tile 12 would fit, 8 measure faster), except two FP8 tiles (two workgroups of 4);
+    # 12 waves stay available on request
     long_ctx = {**ok, "max_context": 2048, "max_blocks_per_seq": 512}
     pl_long = pa.pa_attention_plan(pa.make_desc(**long_ctx), 1)
-    assert pl_long.waves_per_group == 12 and pl_long.tiles_per_wave == 1
+    assert pl_long.waves_per_group == 8 and pl_long.tiles_per_wave == 1
+    assert pa.pa_attention_plan(pa.make_desc(**{**long_ctx, "waves_per_group": 12}), 1).waves_per_group == 12
     pl_long = pa.pa_attention_plan(pa.make_desc(**{**long_ctx, "num_q_heads": 40}), 1)
     assert pl_long.waves_per_group == 8 and pl_long.tiles_per_wave == 2
     pl_long = pa.pa_attention_plan(pa.make_desc(**{**long_ctx, "num_q_heads": 40,
