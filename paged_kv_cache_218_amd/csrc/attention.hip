@@ -223,8 +223,8 @@ __device__ __forceinline__ int out_row(const AttnArgs& a, int b, int g, int r) {
 }
 
 // Cross-wave merge of per-wave online-softmax states kept in LDS, then the
-// final or partial write. m_s/l_s: [W][rows_pad]; o_s: [W][rows_pad][D].
-template <typename T, int D>
+// final or partial write. m_s/l_s: [W][rows_pad]; o_s: [W][rows_pad][O_STRIDE].
+template <typename T, int D, int O_STRIDE = D>
 __device__ void merge_and_store(const AttnArgs& a, const Tile& t, int R, int rows_pad, int W,
                                 const float* m_s, const float* l_s, const float* o_s,
                                 bool poisoned) {
@@ -238,7 +238,7 @@ __device__ void merge_and_store(const AttnArgs& a, const Tile& t, int R, int row
     for (int w = 0; w < W; ++w) {
       const float f = fast_exp2(m_s[w * rows_pad + r] - Mu);
       l += f * l_s[w * rows_pad + r];
-      o += f * o_s[(w * rows_pad + r) * D + c];
+      o += f * o_s[(w * rows_pad + r) * O_STRIDE + c];
     }
     const float val = poisoned ? NAN : (l > 0.f ? o / l : 0.f);
     const int row = out_row(a, t.b, t.g, r);
@@ -806,8 +806,21 @@ __device__ void mfma_wave_steps(const AttnArgs& a, int b, int g, int L, int firs
   }
 }
 
+// Floats per parked row of a partition run: m, the 4 lanes' l, the poisoned
+// flag, 2 unused, the D columns and 4 more, which make the stride (D + 12,
+// 16-byte aligned) step 12 banks a row, so that the 16 rows a row tile
+// writes at once fall in distinct banks (3n mod 16 takes every value).
+__host__ __device__ constexpr int run_slot_row(int D) { return D + 12; }
+
+// Row stride of the parked o rows: D + kParkPad floats. The 16 lanes of a
+// row tile that hold the same columns write 16 rows at once; with a stride of
+// D floats (a multiple of the 64 LDS banks) all 16 land in the same 4 banks,
+// while 4 more floats per row move each row 4 banks on, over all 64.
+constexpr int kParkPad = 4;
+
 // Park each wave's state of the R real rows in LDS (m_s[W][R], l_s[W][R],
-// o_s[W][R][D]) and return whether any wave of the workgroup saw a bad block.
+// o_s[W][R][D + kParkPad]) and return whether any wave of the workgroup saw a
+// bad block.
 template <int D, int NT>
 __device__ bool park_states(const WaveState<D, NT>& st, int R, float* smem) {
   const int W = blockDim.x / 64;
@@ -833,7 +846,7 @@ __device__ bool park_states(const WaveState<D, NT>& st, int R, float* smem) {
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o_s[(wave * R + r) * D + 16 * dt + 4 * j + k] = st.acc[nt][dt][k];
+        for (int k = 0; k < 4; ++k) o_s[(wave * R + r) * (D + kParkPad) + 16 * dt + 4 * j + k] = st.acc[nt][dt][k];
     }
   }
   return __syncthreads_or(st.poisoned ? 1 : 0) != 0;
@@ -870,7 +883,7 @@ __device__ __forceinline__ f32x4 park_chunk(const float* park, int W, int R, int
   const float* o_s = park + 2 * W * R;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int w = 0; w < W; ++w)
-    acc += wt[r * W + w] * *reinterpret_cast<const f32x4*>(o_s + (w * R + r) * D + c);
+    acc += wt[r * W + w] * *reinterpret_cast<const f32x4*>(o_s + (w * R + r) * (D + kParkPad) + c);
   return acc;
 }
 
@@ -890,7 +903,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn(AttnArgs a) {
   mfma_wave_steps<D, BS, NT, STREAM, KV8, TREE>(a, t.b, t.g, t.L, s0 + wave, s1, st,
                                                 [W](int s) { return s + W; });
   const bool bad = park_states(st, R, smem);
-  merge_and_store<uint16_t, D>(a, t, R, R, W, smem, smem + W * R, smem + 2 * W * R, bad);
+  merge_and_store<uint16_t, D, D + kParkPad>(a, t, R, R, W, smem, smem + W * R, smem + 2 * W * R, bad);
 }
 
 // Fixed partitions, one wavefront per partition (chosen when the partitions
@@ -914,7 +927,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn(AttnArgs a) {
 // per partition, bit for bit.
 template <int D, int BS, int NT, bool STREAM, bool KV8, bool TREE, bool RUNS>
 __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void mfma_attn_wave(AttnArgs a) {
-  extern __shared__ float smem[];  // runs: [W][run_parts - 1][R][D + 8] parked states
+  extern __shared__ float smem[];  // runs: [W][run_parts - 1][R][run_slot_row(D)] parked states
   const int W = blockDim.x / 64, wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int n = lane & 15, j = lane >> 4;
   const int R = a.group * a.q_len;
@@ -976,7 +989,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void mfma_attn_wave(AttnArgs 
   // partial keeps, per row, m, the 4 lanes' partial row sums, a poison flag
   // and the raw accumulator; the flush forms l and o = acc / l exactly as
   // emit does.
-  constexpr int kSlotRow = D + 8;  // floats per parked row (16-byte aligned)
+  constexpr int kSlotRow = run_slot_row(D);
   const int spp = a.part_tokens / kStep;  // steps per partition
   const int rpp = (a.parts + a.run_parts - 1) / a.run_parts;  // runs per pair
   const int64_t wid = int64_t(blockIdx.x) * W + wave;
@@ -1602,10 +1615,10 @@ constexpr int kPerCuMinContext = 2048;  // one workgroup per CU once the longest
 
 size_t lds_bytes(const Plan& pl, int D, int num_seqs) {
   if (pl.path == PA_PATH_MFMA) {
-    const size_t park = size_t(pl.waves) * pl.rows * (D + 2) * sizeof(float);
+    const size_t park = size_t(pl.waves) * pl.rows * (D + 2 + kParkPad) * sizeof(float);
     // runs: each wave's parked partials
     if (pl.sched == PA_SCHED_PARTITIONS_WAVE)
-      return size_t(pl.waves) * (pl.run_parts - 1) * pl.rows * (D + 8) * sizeof(float);
+      return size_t(pl.waves) * (pl.run_parts - 1) * pl.rows * run_slot_row(D) * sizeof(float);
     if (pl.sched == PA_SCHED_PARTITIONS) return park;
     return size_t((num_seqs + 1 + 3) & ~3) * sizeof(int32_t) + park;  // step prefix sums, then the park area
   }
@@ -1757,7 +1770,7 @@ pa_status make_plan(const pa_attn_desc* d, int32_t q_len, Plan* pl) {
   if (pl->sched == PA_SCHED_PARTITIONS_WAVE && parts > 1 && pt % kStep == 0) {
     const int per_cu = pl->nt == 1 ? kWavesPerCu : balanced_waves(2);
     const int64_t total = pairs * parts;
-    const size_t slot = size_t(rows) * (d->head_dim + 8) * sizeof(float);
+    const size_t slot = size_t(rows) * run_slot_row(d->head_dim) * sizeof(float);
     const int kmax = 1 + int((kMaxLdsBytes - kStaticLdsReserve) / (size_t(per_cu) * slot));
     const int k = std::min<int64_t>(kmax, (total + int64_t(cus) * per_cu - 1) / (int64_t(cus) * per_cu));
     if (k > 1) {
