@@ -45,3 +45,28 @@ def brute_attention(q, k_pool, v_pool, tables, lens, q_len, scale, block_size, d
             ob.append(oi)
         out.append(ob)
     return out
+
+
+def brute_attention_logical(q, k, v, q_len, scale, dtype):
+    """One sequence from its never-paged K/V: q [q_len][H_q][d]; k, v
+    [L][H_kv][d] in token order. No pool, no block table: this pin shares
+    nothing with the pool layout or the gather. Drafted token i sees
+    positions 0 .. L - q_len + i. Returns nested lists [q_len][H_q][d]."""
+    L, Hkv, d = k.shape
+    Hq = q.shape[1]
+    G = Hq // Hkv
+    out = []
+    for i in range(q_len):
+        oi = []
+        for h in range(Hq):
+            g = h // G
+            qv = [scalar(q[i, h, c], dtype) for c in range(d)]
+            scores = []
+            for t in range(L - q_len + i + 1):
+                scores.append(scale * math.fsum(qv[c] * scalar(k[t, g, c], dtype) for c in range(d)))
+            mx = max(scores)
+            e = [math.exp(s - mx) for s in scores]
+            z = math.fsum(e)
+            oi.append([math.fsum(e[t] * scalar(v[t, g, c], dtype) for t in range(len(e))) / z for c in range(d)])
+        out.append(oi)
+    return out

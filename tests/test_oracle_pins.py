@@ -13,7 +13,7 @@ from oracle import kvbytes, split
 from oracle.build import build_pool
 from oracle.numerics import to_f64
 from oracle.store import HostPool
-from tests.brute import brute_attention
+from tests.brute import brute_attention, brute_attention_logical
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -105,6 +105,29 @@ def test_oracle_vs_brute_force(dtype, q_len, hq, hkv, d, bs, lens):
     got = oatt.attention_paged(w.q_all(), pool, tables, w.lens, q_len, 0.37)
     want = np.array(brute_attention(w.q_all(), pool.k, pool.v, tables, w.lens, q_len, 0.37, bs, dtype))
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("dtype,q_len,hq,hkv,d,bs,lens,prefix", [
+    ("f32", 1, 4, 2, 32, 4, (1, 5, 9), 0),
+    ("bf16", 3, 8, 2, 32, 4, (3, 8, 13), 0),
+    ("bf16", 4, 4, 1, 64, 8, (4, 11, 20), 0),
+    ("bf16", 2, 4, 2, 32, 4, (9, 14), 8),     # two blocks of a shared prefix
+])
+def test_oracle_vs_brute_force_on_never_paged_kv(dtype, q_len, hq, hkv, d, bs, lens, prefix):
+    """The oracle's paged result against a scalar brute force over each
+    sequence's K/V in token order, as the generator drew them: neither the
+    pool's layout nor the block tables enter the reference side."""
+    cfg = workloads.Config("brute", 91, batch=len(lens), q_len=q_len, num_q_heads=hq,
+                           num_kv_heads=hkv, head_dim=d, block_size=bs, dtype=dtype,
+                           lens=lens, prefix_len=prefix, pool_slack=1.5)
+    w = workloads.generate(cfg)
+    pool, _, tables, _ = build_pool(w)
+    got = oatt.attention_paged(w.q_all(), pool, tables, w.lens, q_len, 0.37)
+    for b in range(cfg.batch):
+        k, v = w.logical_kv(b)
+        assert k.shape[0] == w.lens[b]
+        want = np.array(brute_attention_logical(w.seqs[b].q, k, v, q_len, 0.37, dtype))
+        np.testing.assert_allclose(got[b], want, rtol=0, atol=1e-13)
 
 
 # -- torch's fp64 scaled_dot_product_attention on the never-paged K/V ------

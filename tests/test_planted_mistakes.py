@@ -34,6 +34,8 @@ def run_pins():
     checks = {
         "brute": lambda: pins.test_oracle_vs_brute_force("bf16", 4, 4, 1, 64, 8, (4, 11, 20)),
         "brute_gqa": lambda: pins.test_oracle_vs_brute_force("bf16", 1, 8, 2, 32, 4, (3, 8, 13)),
+        "brute_logical": lambda: pins.test_oracle_vs_brute_force_on_never_paged_kv(
+            "bf16", 3, 8, 2, 32, 4, (3, 8, 13), 0),
         "sdpa_verify": lambda: pins.test_oracle_vs_torch_sdpa("prefix_verify"),
         "sdpa_decode": lambda: pins.test_oracle_vs_torch_sdpa("llama3_8b_decode"),
         "tables": lambda: [pins.test_printed_block_tables(c) for c in
