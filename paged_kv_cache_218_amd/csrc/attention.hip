@@ -15,9 +15,10 @@
 //
 // Two schedules:
 //   balanced    (default) the grid is the device's resident capacity; the
-//               (sequence, KV head, step) list is cut into one contiguous
+//               (KV head, sequence, step) list is cut into one contiguous
 //               range per workgroup, equal in steps (prefix sums of the
-//               steps computed in every workgroup from context_lens). A
+//               steps computed in every workgroup from context_lens), the
+//               ranges of one XCD consecutive (so it holds whole KV heads). A
 //               segment inside one range is written directly; a segment cut
 //               by range boundaries leaves (m, l, o) partials, and the
 //               workgroup that counts the last piece in merges them with the
@@ -1076,6 +1077,7 @@ constexpr int kMergeBatch = 8;   // pieces whose partial loads a thread has in f
 // is counted as work by the balanced partition, in steps (Plan::seg_cost),
 // so that ranges holding many short segments get fewer steps.
 constexpr int kMinGroupSteps = 8;  // fewest steps a workgroup's range holds
+constexpr int kXcds = 8;           // accelerator complex dies (each with its own L2)
 
 // The workgroup that completed a segment merges its npieces partials, which
 // start at piece p0 (log-sum-exp identity: out = sum_p w_p o_p / sum_p w_p
@@ -1173,10 +1175,14 @@ __global__ __launch_bounds__(64 * balanced_waves(NT)) void mfma_attn_balanced(At
     if (B <= tid * chunk && tid == 0) pre[B] = 0;
     __syncthreads();
   }
-  const int64_t k = blockIdx.x;
-  const int64_t S = int64_t(pre[B]) * a.hkv;
+  // Units in head-major order: KV head g's segments fill [g P, (g + 1) P),
+  // P = pre[B], sequence b's segment [g P + pre[b], g P + pre[b + 1]).
+  // Segments are numbered in the same order (seg = g B + b) for the arrival
+  // counters and the partials.
+  const int64_t P = pre[B];
+  const int64_t S = P * a.hkv;
   // sequences with an out-of-range length: NaN rows, spread over the grid
-  for (int b = int(k); b < B; b += int(gridDim.x)) {
+  for (int b = int(blockIdx.x); b < B; b += int(gridDim.x)) {
     const int L = a.lens[b];
     if (L < a.q_len || L > a.max_ctx)
       for (int e = threadIdx.x; e < a.q_len * a.hq * D; e += blockDim.x)
@@ -1186,15 +1192,23 @@ __global__ __launch_bounds__(64 * balanced_waves(NT)) void mfma_attn_balanced(At
   // pieces of a segment are exactly the workgroups from its first owner to
   // its last.
   const int64_t N = min(int64_t(gridDim.x), (S + kMinGroupSteps - 1) / kMinGroupSteps);
-  if (k >= N) return;
+  if (int64_t(blockIdx.x) >= N) return;
+  // Range k of workgroup blockIdx.x. Workgroups go to the XCDs in turn
+  // (workgroup i to XCD i mod kXcds): with N a multiple of kXcds, each XCD
+  // takes N / kXcds consecutive ranges, i.e. whole KV heads, so that blocks
+  // several sequences share (a common prompt) are fetched into its L2 once
+  // and then read there by the XCD's other workgroups.
+  const int64_t k = N % kXcds == 0 ? int64_t(blockIdx.x % kXcds) * (N / kXcds) + blockIdx.x / kXcds
+                                   : int64_t(blockIdx.x);
   const int64_t x0 = range_start(k, S, N), x1 = range_start(k + 1, S, N);
-  // first sequence whose segments reach past x0
-  int b = 0;
+  // the head and the first sequence whose segment reaches past x0
+  int g = int(x0 / P), b = 0;
   {
-    int lo = 0, hi = B - 1;  // largest b with hkv * pre[b] <= x0
+    const int64_t xr = x0 - int64_t(g) * P;
+    int lo = 0, hi = B - 1;  // largest b with pre[b] <= xr
     while (lo < hi) {
       const int mid = (lo + hi + 1) / 2;
-      if (int64_t(pre[mid]) * a.hkv <= x0) lo = mid; else hi = mid - 1;
+      if (pre[mid] <= xr) lo = mid; else hi = mid - 1;
     }
     b = lo;
   }
@@ -1208,11 +1222,14 @@ __global__ __launch_bounds__(64 * balanced_waves(NT)) void mfma_attn_balanced(At
   // a segment whose start units it ends in).
   int64_t x = x0;
   while (x < x1) {
-    const int nu = pre[b + 1] - pre[b];  // units of each segment of sequence b
-    if (nu == 0 || int64_t(pre[b + 1]) * a.hkv <= x) { ++b; continue; }
-    const int64_t seq_start = int64_t(pre[b]) * a.hkv;
-    const int g = int((x - seq_start) / nu);
-    const int64_t seg_start = seq_start + int64_t(g) * nu, seg_end = seg_start + nu;
+    if (b >= B) {  // on to the next head
+      ++g;
+      b = 0;
+      continue;
+    }
+    const int nu = pre[b + 1] - pre[b];  // units of sequence b's segment
+    const int64_t seg_start = int64_t(g) * P + pre[b], seg_end = seg_start + nu;
+    if (nu == 0 || seg_end <= x) { ++b; continue; }
     const int64_t real_start = seg_start + a.seg_cost;  // unit of the segment's first step
     const int nb = nu - a.seg_cost;
     if (min(x1, seg_end) <= real_start) { x = min(x1, seg_end); continue; }  // only start units here
@@ -1223,7 +1240,7 @@ __global__ __launch_bounds__(64 * balanced_waves(NT)) void mfma_attn_balanced(At
     mfma_wave_steps<D, BS, NT, STREAM, KV8, TREE>(a, b, g, L, first + wave, last, st,
                                                   [W](int s) { return s + W; });
     const bool bad = park_states(st, R, park);
-    const int64_t seg = int64_t(b) * a.hkv + g;
+    const int64_t seg = int64_t(g) * B + b;
     const bool whole = first == 0 && last == nb;
     uint16_t* out = static_cast<uint16_t*>(a.out);
     __shared__ float wt[kMfmaMaxRows * 16], row_ml[kMfmaMaxRows * 2];  // per-row wave weights, (M, l)
@@ -1275,7 +1292,7 @@ __global__ __launch_bounds__(64 * balanced_waves(NT)) void mfma_attn_balanced(At
   // partial, so at most two), kept out of the step loop's registers.
   for (int d = 0; d < n_duty; ++d) {
     const int64_t seg = duty_seg[d];
-    const int bb = int(seg / a.hkv), gg = int(seg % a.hkv);
+    const int bb = int(seg % B), gg = int(seg / B);
     merge_pieces<D>(a, duty_p0[d], duty_n[d], R,
                     static_cast<uint16_t*>(a.out) + int64_t(out_row(a, bb, gg, 0)) * D);
     if (threadIdx.x == 0)  // ready for the next call
