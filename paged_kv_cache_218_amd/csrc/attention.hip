@@ -1663,7 +1663,7 @@ int default_waves(const Plan& pl, int max_context) {
 // measured optimum per pool format: an FP8 step moves half the bytes, so a
 // boundary weighs more steps).
 int default_segment_cost(const Plan& pl) {
-  return pl.kv8 ? 16 : 12;
+  return pl.kv8 ? 16 : 8;
 }
 
 // Compute units of the current device, queried once per device and kept
