@@ -287,6 +287,12 @@ typedef struct pa_attn_plan {
                                  KV head) each wavefront streams: 1, or a run of several
                                  when the partitions outnumber the device's wave slots;
                                  0 for the other schedules */
+  int32_t segment_cost;       /* BALANCED: steps a (sequence, KV head) segment's start
+                                 counts for when the (KV head, sequence, step) list is
+                                 cut into equal ranges: S = H_kv * sum over valid
+                                 sequences of (ceil(L/32) + segment_cost) units, and
+                                 min(grid, ceil(S / 8)) ranges; 0 for the other
+                                 schedules */
   size_t workspace_bytes;     /* workspace pa_attention needs */
 } pa_attn_plan;
 

@@ -34,7 +34,8 @@ class AttnDesc(C.Structure):
 class AttnPlan(C.Structure):
     _fields_ = [("path", i32), ("schedule", i32), ("partition_tokens", i32), ("num_partitions", i32),
                 ("waves_per_group", i32), ("grid", i32), ("merge_grid", i32),
-                ("tiles_per_wave", i32), ("partitions_per_wave", i32), ("workspace_bytes", sz)]
+                ("tiles_per_wave", i32), ("partitions_per_wave", i32), ("segment_cost", i32),
+                ("workspace_bytes", sz)]
 
 
 # (name, restype, argtypes) of every exported entry point

@@ -1933,6 +1933,7 @@ extern "C" pa_status pa_attention_plan(const pa_attn_desc* desc, int32_t q_len, 
   out->merge_grid = pl.merge_grid;
   out->tiles_per_wave = pl.path == PA_PATH_MFMA ? pl.nt : 0;
   out->partitions_per_wave = pl.sched == PA_SCHED_PARTITIONS_WAVE ? pl.run_parts : 0;
+  out->segment_cost = pl.sched == PA_SCHED_BALANCED ? pl.seg_cost : 0;
   out->workspace_bytes = pl.ws;
   return PA_OK;
 }

@@ -227,6 +227,8 @@ def test_attention_plan_validation():
     pl_long = pa.pa_attention_plan(pa.make_desc(**{**long_ctx, "num_q_heads": 40,
                                                   "kv_format": pa.PA_KV_FP8_E4M3}), 1)
     assert pl_long.waves_per_group == 4 and pl_long.tiles_per_wave == 2
+    # a segment's start counts for 8 steps over bf16 pools, 16 over FP8 (half the bytes a step)
+    assert pl.segment_cost == 8 and pl_long.segment_cost == 16
     assert pa.pa_attention_plan(pa.make_desc(**{**long_ctx, "max_context": 2047}), 1).waves_per_group == 4
     assert pa.pa_attention_plan(pa.make_desc(**{**long_ctx, "num_q_heads": 40, "waves_per_group": 8}),
                                 1).waves_per_group == 8
@@ -238,7 +240,7 @@ def test_attention_plan_validation():
     assert e.value.status == _lib.PA_ERR_UNSUPPORTED
     assert pl.workspace_bytes == pa.pa_attention_workspace_size(pa.make_desc(**ok), 1) > 0
     pl = pa.pa_attention_plan(pa.make_desc(**{**ok, "partition_tokens": 64}), 1)
-    assert pl.schedule == _lib.PA_SCHED_PARTITIONS and pl.num_partitions == 2
+    assert pl.schedule == _lib.PA_SCHED_PARTITIONS and pl.num_partitions == 2 and pl.segment_cost == 0
     pl = pa.pa_attention_plan(pa.make_desc(**{**ok, "path": pa.PA_PATH_VALU}), 1)
     assert pl.schedule == _lib.PA_SCHED_PARTITIONS
     # partitions that fill the device's 3072 wave slots on their own: one wavefront each,

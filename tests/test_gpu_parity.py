@@ -307,3 +307,49 @@ def test_bad_lengths_and_tables_give_nan_not_faults():
             o = out_to_f64(out, "bf16")
             assert np.isnan(o[1]).all() and np.isnan(o[2]).all() and np.isnan(o[3]).all()
             assert np.isfinite(o[[0, 4]]).all()
+
+
+def _num_ranges(w, cache):
+    """Ranges the balanced schedule cuts the (KV head, sequence, step) list
+    into: min(grid, ceil(S / 8)), S = H_kv * sum of (ceil(L / 32) + segment
+    cost) over the sequences (the plan's documented partition)."""
+    import paged_kv_cache_218_amd as pa
+    cfg = w.cfg
+    pl = pa.pa_attention_plan(cache.desc(cfg.num_q_heads, int(w.lens.max()), MFMA), cfg.q_len)
+    assert pl.schedule == pa.PA_SCHED_BALANCED and pl.segment_cost > 0
+    units = sum(-(-int(L) // 32) + pl.segment_cost for L in w.lens)
+    return min(pl.grid, -(-units * cfg.num_kv_heads // 8))
+
+
+RANGE_CASES = [
+    # (workload, overrides, whether the number of ranges is a multiple of 8, so
+    # that each XCD takes consecutive ranges, i.e. whole KV heads)
+    ("llama3_8b_decode", dict(batch=8, len_const=600), True),
+    ("llama3_8b_decode", dict(batch=5, len_const=333), False),
+    ("llama3_8b_decode", dict(batch=8, len_const=600, kv_dtype="fp8"), True),
+    ("llama3_8b_decode", dict(batch=3, len_const=0, lens=(40, 333, 700), kv_dtype="fp8"), False),
+    ("prefix_verify", dict(batch=8, prefix_len=64, len_lo=40, len_hi=500), None),
+    ("tree_verify", dict(batch=6, prefix_len=32, len_lo=20, len_hi=400), None),
+]
+
+
+@pytest.mark.parametrize("name,kw,grouped", RANGE_CASES, ids=[f"{n}-{i}" for i, (n, _, _) in enumerate(RANGE_CASES)])
+def test_balanced_range_to_workgroup_mapping(name, kw, grouped):
+    """Ranges go to workgroups grouped by XCD when their number is a multiple
+    of 8, one to one otherwise; both give the oracle's rows, and the batch's
+    unit order (KV head major) covers every (sequence, KV head) exactly once."""
+    from paged_kv_cache_218_amd.cache import PagedKVCache, tree_masks_to_device
+    w = workloads.generate(workloads.config(name, **kw))
+    cache = PagedKVCache.from_workload(w)
+    n = _num_ranges(w, cache)
+    print(f"{name} {kw}: {n} ranges", flush=True)
+    if grouped is not None:
+        assert (n % 8 == 0) == grouped, n
+    tm = None if w.tree_parents is None else tree_masks_to_device(w.tree_parents)
+    out, _ = run_gpu(w, path=MFMA, cache=cache, tree_mask=tm)
+    if w.tree_parents is None:
+        ref = oracle_out(w)
+    else:
+        rows = oracle_rows(w, range(w.cfg.batch))
+        ref = np.stack([rows[b] for b in range(w.cfg.batch)])
+    assert_close(out_to_f64(out, w.cfg.dtype), ref, w.cfg.dtype, f"{name} {n} ranges")
