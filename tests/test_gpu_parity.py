@@ -307,6 +307,15 @@ def test_bad_lengths_and_tables_give_nan_not_faults():
             o = out_to_f64(out, "bf16")
             assert np.isnan(o[1]).all() and np.isnan(o[2]).all() and np.isnan(o[3]).all()
             assert np.isfinite(o[[0, 4]]).all()
+    # no valid sequence at all: nothing to split, every row NaN
+    lens[:] = 0
+    lens[0] = int(w.lens.max()) + 1
+    for path in (MFMA, VALU):
+        for pt in (0, 128):
+            out = cache.attention(torch.from_numpy(w.q_all().view(np.int16)).view(torch.bfloat16).cuda(),
+                                  tables, lens, 1, w.cfg.scale, int(w.lens.max()), path=path, partition_tokens=pt)
+            torch.cuda.synchronize()
+            assert np.isnan(out_to_f64(out, "bf16")).all(), (path, pt)
 
 
 def _num_ranges(w, cache):
